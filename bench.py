@@ -1,0 +1,259 @@
+"""Throughput bench of the attention forward pass on one MI355X.
+
+One step is one fa_fwd launch (the whole forward pass) over the resident
+inputs of the headline workload: causal bf16 attention, B=2, H=32, N=4096,
+d=128 (seeded synthetic data).  Prints one JSON line.
+
+  python bench.py [--steps K] [--warmup W] [--config c3] [--no-cpu-baseline]
+
+FLOPs per launch are the nominal 4*B*H*N^2*d, halved for causal.  The roofline
+entry compares the average launch duration (HIP events around every launch on
+the launch stream, inside the timed region) with the bf16 dense MFMA peak.
+The cpu_baseline entry times the fp64 oracle on a bounded sample of whole
+heads of the same workload on the host cores.
+
+Profiling helpers (for rocprofv3 runs of this same script):
+  --calibrate-copy       also launch a plain elementwise copy of known size
+                         (for scaling FETCH_SIZE / WRITE_SIZE counters)
+  --summarize DIR        print per-kernel figures from rocprofv3 output in DIR
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOP/s (bf16, causal, N=4096 d=128) + % of MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+KERNEL_SRC = os.path.join(ROOT, "io_aware_tiled_04_amd", "csrc", "fa_fwd_bf16.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_bf16_c3_hbm_traffic.md")
+COPY_BYTES = 512 << 20
+
+
+def kernel_sha() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic():
+    """HBM bytes per launch from the committed counter summary, or None when
+    the kernel source changed since the counters were taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    fields = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and line.strip().startswith("- "):
+            key, _, val = line.strip()[2:].partition(":")
+            fields[key.strip()] = val.strip().strip("`")
+    if fields.get("kernel_source_sha256_16") != kernel_sha():
+        return None
+    try:
+        return float(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, q, k, v, budget_s: float):
+    """The oracle as it stands, on whole (batch, head) units of the workload,
+    in order, until all are done or about ``budget_s`` seconds have passed."""
+    import numpy as np
+    import oracle
+    from io_aware_tiled_04_amd.workloads import as_f64_numpy
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()
+                       if p.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    q64 = as_f64_numpy(q)
+    k64 = as_f64_numpy(k)
+    v64 = as_f64_numpy(v)
+    g = w.Hq // w.Hkv
+    per_head = w.nominal_flops() / (w.B * w.Hq)
+    heads, t0 = 0, time.perf_counter()
+    while heads < w.B * w.Hq and (time.perf_counter() - t0) < budget_s:
+        b, h = divmod(heads, w.Hq)
+        o, lse = oracle.attention_head(q64[b, h], k64[b, h // g], v64[b, h // g], w.scale,
+                                       w.causal)
+        assert np.all(np.isfinite(o))
+        heads += 1
+    dt = time.perf_counter() - t0
+    return {"value": per_head * heads / dt / 1e12, "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{heads} of {w.B * w.Hq} whole (batch, head) units of {w.name}, "
+                      f"N={w.N} d={w.d}, "
+                      f"fp64 numpy, {dt:.1f} s; nominal FLOPs as for the GPU "
+                      f"(the oracle computes all N^2 scores)"}
+
+
+def summarize(d: str) -> None:
+    """Per-kernel figures from a rocprofv3 output directory (its rocpd SQLite
+    database): average dispatch duration from a kernel trace, and per-dispatch
+    counter values from a --pmc run, with the FETCH_SIZE / WRITE_SIZE scale
+    factors implied by the elementwise copy of --calibrate-copy (which reads
+    and writes COPY_BYTES each)."""
+    import sqlite3
+    for path in sorted(glob.glob(os.path.join(d, "**", "*_results.db"), recursive=True)):
+        con = sqlite3.connect(path)
+        views = {r[0] for r in con.execute("select name from sqlite_master")}
+        print(f"# {os.path.relpath(path, d)}")
+        if "kernels" in views:
+            for name, n, avg, mn, mx in con.execute(
+                    "select name, count(*), avg(duration), min(duration), max(duration) "
+                    "from kernels group by name order by sum(duration) desc"):
+                print(f"trace | {name[:80]} | calls={n} avg_us={avg / 1e3:.2f} "
+                      f"min_us={mn / 1e3:.2f} max_us={mx / 1e3:.2f}")
+        if "counters_collection" in views:
+            rows = list(con.execute(
+                "select kernel_name, counter_name, count(*), avg(value), min(value), max(value) "
+                "from counters_collection group by kernel_name, counter_name"))
+            copy_kib = COPY_BYTES / 1024
+            factors = {}
+            for kname, cname, n, avg, mn, mx in rows:
+                if "vectorized_elementwise_kernel" in kname and "MulFunctor" in kname or \
+                        ("AUnaryFunctor" in kname and cname in ("FETCH_SIZE", "WRITE_SIZE")):
+                    factors[cname] = copy_kib / avg
+            for kname, cname, n, avg, mn, mx in rows:
+                f = factors.get(cname)
+                extra = f" scale={f:.4f} scaled_bytes={avg * 1024 * f:.6g}" if f else ""
+                print(f"pmc | {kname[:80]} | {cname} dispatches={n} avg_kib={avg:.6g} "
+                      f"min={mn:.6g} max={mx:.6g}{extra}")
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="c3")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--summarize", default=None)
+    args = ap.parse_args()
+
+    if args.summarize:
+        summarize(args.summarize)
+        return 0
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this forward pass shards over (batch, head) "
+              "units with no communication, so run it with --gpus 1 (one process per GPU).",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import oracle
+    from io_aware_tiled_04_amd import fa
+    from io_aware_tiled_04_amd.workloads import CONFIGS, as_f64_numpy, make_inputs
+
+    w = CONFIGS[args.config]
+    if w.dtype != "bf16":
+        print("the bench times the bf16 entry point; pick a bf16 configuration", file=sys.stderr)
+        return 2
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q, k, v = make_inputs(w)
+    qd, kd, vd = (t.to(dev) for t in (q, k, v))
+    o = torch.empty_like(qd)
+    lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    ptrs = (qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(), lse.data_ptr())
+
+    def launch():
+        rc = fa.fa_fwd(*ptrs, w.B, w.Hq, w.Hkv, w.N, w.d, int(w.causal), w.scale,
+                       stream.cuda_stream)
+        if rc != fa.FA_OK:
+            raise fa.FaError(rc)
+
+    for _ in range(args.warmup):
+        launch()
+    torch.cuda.synchronize()
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    region0 = torch.cuda.Event(enable_timing=True)
+    region1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    region0.record(stream)
+    for i in range(args.steps):
+        starts[i].record(stream)
+        launch()
+        ends[i].record(stream)
+    region1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = region0.elapsed_time(region1)
+    launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    avg_launch_ms = sum(launch_ms) / len(launch_ms)
+
+    if args.calibrate_copy:
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+
+    # parity of the timed outputs on sampled rows (oracle row by row)
+    rng = np.random.default_rng(0)
+    rows = [(b, h, int(i)) for b in range(w.B) for h in range(w.Hq)
+            for i in [0, w.N - 1] + list(rng.integers(0, w.N, 2))]
+    q64, k64, v64 = as_f64_numpy(q), as_f64_numpy(k), as_f64_numpy(v)
+    o_ref, lse_ref = oracle.attention_rows(q64, k64, v64, w.causal, w.scale, rows)
+    idx = tuple(np.array(rows).T)
+    o_got = as_f64_numpy(o)[idx]
+    lse_got = as_f64_numpy(lse)[idx]
+    err = np.abs(o_got - o_ref)
+    lerr = np.abs(lse_got - lse_ref)
+    parity_ok = bool(err.max() <= 2e-2 and err.mean() <= 2e-3 and lerr.max() <= 1e-3)
+
+    flops = w.nominal_flops()
+    value = flops * args.steps / (total_ms * 1e-3) / 1e12
+    achieved = flops / (avg_launch_ms * 1e-3) / 1e12
+    traffic = read_traffic()
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(total_ms / args.steps, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: {w.note}", "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv,
+                   "N": w.N, "d": w.d, "causal": w.causal, "seed": w.seed,
+                   "scale": w.scale, "flops_per_step": flops},
+        "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                     "kernel": "fwd_bf16_kernel<128, causal>",
+                     "avg_launch_us": round(avg_launch_ms * 1e3, 2),
+                     "min_launch_us": round(min(launch_ms) * 1e3, 2)},
+        "parity": {"rows": len(rows), "max_abs_o": float(err.max()),
+                   "mean_abs_o": float(err.mean()), "max_abs_lse": float(lerr.max()),
+                   "ok": parity_ok},
+        "wall_s_timed": round(wall, 4),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+    return 0 if parity_ok else 1
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,105 @@
+/*
+ * fa.h - C ABI of the FlashAttention forward pass for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * The operation is exact softmax attention, computed tile by tile so that the
+ * N x N score and probability matrices never reach device memory:
+ *
+ *   O   = softmax(scale * Q K^T, masked) V
+ *   LSE = ln sum_{j allowed} exp(scale * q_i . k_j)       (natural log, fp32)
+ *
+ * Sources for the definition (the three pages on FlashAttention):
+ *  - the derivation blog ("Flash Attention介绍"), section 标准注意力 / 前向传播:
+ *    O = Diag((exp(QK^T) (.) M) 1)^-1 (exp(QK^T) (.) M) V with M causal or
+ *    absent (section 分块递推模式);
+ *  - the reading-notes page, Background (S = QK^T, P = softmax(S), O = PV, per
+ *    head, Q, K, V in R^{N x d}) and Methods (Q resident on chip, K/V read in
+ *    blocks, running sum and output rescaled at each block);
+ *  - the blog's backward section (comment under 梯度推导): the forward keeps
+ *    the row max and row sum for the backward pass, delivered here as LSE;
+ *  - the Polish notes, closing paragraph: grouped-query attention combines
+ *    with the method (fewer K/V heads than query heads).
+ *
+ * Conventions shared by every entry point
+ *  - Layout: q and o are [B, Hq, N, d], k and v are [B, Hkv, N, d], all
+ *    contiguous row-major; lse is [B, Hq, N] float32.  Queries and keys have
+ *    the same length N.  There are no stride arguments.
+ *  - Grouped-query attention: query head hq reads K/V head hq / (Hq / Hkv)
+ *    (contiguous groups); Hq must be a multiple of Hkv.  Hkv == Hq is plain
+ *    multi-head attention.
+ *  - causal != 0: key j is visible to query i iff j <= i.  Masked pairs get
+ *    weight exactly zero.  Every query sees at least key 0, so no row is empty.
+ *  - scale multiplies Q K^T before the mask and the softmax; any finite value
+ *    (negative and zero included).  Results are finite as long as
+ *    |scale * q_i . k_j| stays below about 1e38.
+ *  - All pointers are device pointers (hipMalloc'd or equivalent), owned by the
+ *    caller; the library allocates nothing, frees nothing and keeps no state
+ *    between calls, so it is reentrant and thread-safe.  Outputs must not
+ *    alias inputs.
+ *  - Asynchronous: the work is enqueued on `stream` (NULL = the default
+ *    stream) and the call returns without synchronising.  The caller orders
+ *    and synchronises as for any kernel launch.
+ *  - Errors: arguments are validated before any HIP call; on a validation
+ *    error nothing is launched and the outputs are untouched.  FA_ERR_HIP
+ *    reports a launch failure (for example no gfx950 device).  Faults inside
+ *    the kernel surface on the caller's next synchronising HIP call.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum fa_status {
+    FA_OK = 0,
+    FA_ERR_NULL = -1,      /* a null pointer argument (lse included) */
+    FA_ERR_SHAPE = -2,     /* B, Hq, Hkv or N <= 0, or the problem is too large to index */
+    FA_ERR_HEADS = -3,     /* Hq is not a multiple of Hkv */
+    FA_ERR_HEADDIM = -4,   /* d is not one of the supported head sizes (64, 128) */
+    FA_ERR_ARG = -5,       /* scale is not finite */
+    FA_ERR_HIP = -6        /* the HIP runtime rejected the launch */
+};
+
+/*
+ * fa_fwd - attention forward pass on bfloat16 inputs (the hot path).
+ *
+ * q [B,Hq,N,d], k [B,Hkv,N,d], v [B,Hkv,N,d]: bfloat16 device pointers.
+ * o [B,Hq,N,d]: bfloat16 device pointer, written with O rounded to nearest
+ *   even from its fp32 value.
+ * lse [B,Hq,N]: float32 device pointer, written with the natural-log
+ *   logsumexp of the scaled, masked scores of each query row.
+ * d in {64, 128}; N >= 1 (any length; partial tiles are masked).
+ * Products Q K^T and P V run on bf16 matrix cores with fp32 accumulation; the
+ * softmax state (row max, row sum, output accumulator) is fp32.  The row sum
+ * is taken over the fp32 probabilities before they are rounded to bf16 for
+ * the P V product.
+ * Returns FA_OK or a negative fa_status.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+           hipStream_t stream);
+
+/*
+ * fa_fwd_f32 - the same operation on float32 inputs and output, with fp32
+ * arithmetic throughout (no reduced-precision rounding of P or O).
+ * Arguments, layouts, errors and stream behaviour as for fa_fwd.
+ */
+int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+               int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+               hipStream_t stream);
+
+/*
+ * fa_status_string - a static, human-readable description of a status code
+ * returned by the entry points above ("unknown status" for anything else).
+ * The string is owned by the library and must not be freed.
+ */
+const char* fa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

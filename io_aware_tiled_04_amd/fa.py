@@ -1,0 +1,119 @@
+"""Thin Python binding of the C ABI in include/fa.h (ctypes).
+
+Only argument marshalling lives here: every step of the forward pass runs in
+the HIP kernels of ``libfa.so``.  There is no fallback: if the library is
+missing or cannot be loaded, importing this module raises.
+
+``fa_fwd``, ``fa_fwd_f32`` and ``fa_status_string`` have the C names and
+arguments (integer device pointers, sizes, stream handle).  ``fwd`` is the
+torch-facing convenience: it checks the tensors, allocates O and LSE on the
+inputs' device and launches on torch's current stream.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libfa.so")
+
+FA_OK = 0
+FA_ERR_NULL = -1
+FA_ERR_SHAPE = -2
+FA_ERR_HEADS = -3
+FA_ERR_HEADDIM = -4
+FA_ERR_ARG = -5
+FA_ERR_HIP = -6
+
+# Names declared in include/fa.h, in order.
+EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_status_string")
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m io_aware_tiled_04_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(LIB_PATH)
+    fwd_args = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 6 + \
+        [ctypes.c_float, ctypes.c_void_p]
+    for name in ("fa_fwd", "fa_fwd_f32"):
+        fn = getattr(lib, name)
+        fn.argtypes = fwd_args
+        fn.restype = ctypes.c_int
+    lib.fa_status_string.argtypes = [ctypes.c_int]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    return lib
+
+
+_lib = _load()
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int):
+        self.status = status
+        super().__init__(f"fa status {status}: {fa_status_string(status)}")
+
+
+def fa_status_string(status: int) -> str:
+    return _lib.fa_status_string(int(status)).decode()
+
+
+def fa_fwd(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, stream) -> int:
+    """Raw call of the C entry point; pointers and stream are integers."""
+    return _lib.fa_fwd(q, k, v, o, lse, B, Hq, Hkv, N, d, int(causal), float(scale), stream)
+
+
+def fa_fwd_f32(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, stream) -> int:
+    """Raw call of the fp32 C entry point; pointers and stream are integers."""
+    return _lib.fa_fwd_f32(q, k, v, o, lse, B, Hq, Hkv, N, d, int(causal), float(scale), stream)
+
+
+def _check(t, name, dtype, device):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device != device or t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU device {device}")
+    if t.dim() != 4:
+        raise ValueError(f"{name} must be 4-D [B, H, N, d]")
+
+
+def fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse_out=None,
+        stream=None):
+    """Attention forward: returns (O, LSE).
+
+    q [B,Hq,N,d], k/v [B,Hkv,N,d]: contiguous bf16 (or fp32) device tensors.
+    O has q's dtype and shape; LSE is fp32 [B,Hq,N].  ``scale`` defaults to
+    1/sqrt(d).  Launches on ``stream`` (a torch stream) or torch's current
+    stream, without synchronising.
+    """
+    import torch
+    dev = q.device
+    dtype = q.dtype
+    if dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("q must be bfloat16 or float32")
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, n, dtype, dev)
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    if tuple(k.shape) != (B, Hkv, N, d) or tuple(v.shape) != (B, Hkv, N, d):
+        raise ValueError("k and v must be [B, Hkv, N, d] with q's B, N and d")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev) if lse_out is None else lse_out
+    _check(o, "out", dtype, dev)
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != (B, Hq, N):
+        raise ValueError("lse_out must be a contiguous fp32 [B, Hq, N] tensor")
+    s = (stream if stream is not None else torch.cuda.current_stream(dev)).cuda_stream
+    fn = fa_fwd if dtype == torch.bfloat16 else fa_fwd_f32
+    rc = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+            B, Hq, Hkv, N, d, causal, scale, s)
+    if rc != FA_OK:
+        raise FaError(rc)
+    return o, lse

@@ -1,0 +1,105 @@
+"""The C ABI without a GPU: the library loads, exports every entry point that
+include/fa.h declares, and rejects every invalid argument before any HIP call
+(so these calls are safe on a machine with no device)."""
+import ctypes
+import importlib
+import math
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(fa_\w+)\s*\(", text, flags=re.M)
+
+
+def test_header_declares_the_entry_points():
+    assert _declared() == ["fa_fwd", "fa_fwd_f32", "fa_status_string"]
+
+
+def test_library_exports_every_declared_symbol():
+    from io_aware_tiled_04_amd import fa
+    lib = ctypes.CDLL(fa.LIB_PATH)
+    for name in _declared():
+        assert hasattr(lib, name), name
+    assert tuple(_declared()) == fa.EXPORTS
+
+
+def test_status_codes_match_header():
+    from io_aware_tiled_04_amd import fa
+    text = open(HEADER).read()
+    for name, val in re.findall(r"(FA_\w+)\s*=\s*(-?\d+)", text):
+        assert getattr(fa, name) == int(val)
+        assert fa.fa_status_string(int(val)) != "unknown status"
+    assert fa.fa_status_string(12345) == "unknown status"
+
+
+# Fake non-null "pointers": validation rejects these calls before any use.
+P = 0x1000
+
+
+@pytest.mark.parametrize("fn", ["fa_fwd", "fa_fwd_f32"])
+@pytest.mark.parametrize("args,expect", [
+    ((0, P, P, P, P, 1, 1, 1, 128, 64, 0, 0.125), "FA_ERR_NULL"),
+    ((P, 0, P, P, P, 1, 1, 1, 128, 64, 0, 0.125), "FA_ERR_NULL"),
+    ((P, P, 0, P, P, 1, 1, 1, 128, 64, 0, 0.125), "FA_ERR_NULL"),
+    ((P, P, P, 0, P, 1, 1, 1, 128, 64, 0, 0.125), "FA_ERR_NULL"),
+    ((P, P, P, P, 0, 1, 1, 1, 128, 64, 0, 0.125), "FA_ERR_NULL"),
+    ((P, P, P, P, P, 0, 1, 1, 128, 64, 0, 0.125), "FA_ERR_SHAPE"),
+    ((P, P, P, P, P, 1, 0, 1, 128, 64, 0, 0.125), "FA_ERR_SHAPE"),
+    ((P, P, P, P, P, 1, 1, 0, 128, 64, 0, 0.125), "FA_ERR_SHAPE"),
+    ((P, P, P, P, P, 1, 1, 1, 0, 64, 0, 0.125), "FA_ERR_SHAPE"),
+    ((P, P, P, P, P, 1, 1, 1, -5, 64, 0, 0.125), "FA_ERR_SHAPE"),
+    ((P, P, P, P, P, 65536, 65536, 1, 4096, 64, 0, 0.125), "FA_ERR_SHAPE"),
+    ((P, P, P, P, P, 1, 6, 4, 128, 64, 1, 0.125), "FA_ERR_HEADS"),
+    ((P, P, P, P, P, 1, 1, 1, 128, 96, 1, 0.125), "FA_ERR_HEADDIM"),
+    ((P, P, P, P, P, 1, 1, 1, 128, 256, 1, 0.125), "FA_ERR_HEADDIM"),
+    ((P, P, P, P, P, 1, 1, 1, 128, 64, 1, math.nan), "FA_ERR_ARG"),
+    ((P, P, P, P, P, 1, 1, 1, 128, 64, 1, math.inf), "FA_ERR_ARG"),
+    ((P, P, P, P, P, 1, 1, 1, 128, 64, 1, -math.inf), "FA_ERR_ARG"),
+])
+def test_invalid_arguments_are_rejected(fn, args, expect):
+    from io_aware_tiled_04_amd import fa
+    rc = getattr(fa, fn)(*args, 0)
+    assert rc == getattr(fa, expect), (rc, fa.fa_status_string(rc))
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """No silent fallback: without libfa.so the binding refuses to load."""
+    from io_aware_tiled_04_amd import fa
+    monkeypatch.setattr(fa, "LIB_PATH", str(tmp_path / "libfa.so"))
+    with pytest.raises(ImportError):
+        fa._load()
+
+
+def test_product_path_does_not_import_the_oracle():
+    """The package never imports the oracle (test infrastructure only)."""
+    pkg = os.path.join(ROOT, "io_aware_tiled_04_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                src = open(os.path.join(dirpath, f), encoding="utf-8").read()
+                assert not re.search(r"^\s*(from|import)\s+oracle\b", src, flags=re.M), f
+                assert "oracle/" not in src, f
+
+
+def test_workloads_are_seeded_and_shaped():
+    from io_aware_tiled_04_amd.workloads import CONFIGS, make_inputs
+    import torch
+    w = CONFIGS["c5"].with_(N=64)
+    q, k, v = make_inputs(w)
+    assert q.shape == (1, 32, 64, 128) and k.shape == (1, 8, 64, 128)
+    assert q.dtype == torch.bfloat16 and q.is_contiguous()
+    q2, _, _ = make_inputs(w)
+    assert torch.equal(q, q2)
+    c4 = CONFIGS["c4"].with_(N=512)
+    q, k, v = make_inputs(c4)
+    assert 1.8 < q.float().std().item() < 2.2 and 0.9 < v.float().std().item() < 1.1
+    assert CONFIGS["c1"].dtype == "f32" and make_inputs(CONFIGS["c1"])[0].dtype == torch.float32
+    assert CONFIGS["c3"].nominal_flops() == 4 * 2 * 32 * 4096 ** 2 * 128 / 2
