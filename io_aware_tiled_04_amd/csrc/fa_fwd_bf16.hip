@@ -1,11 +1,11 @@
 // Attention forward pass, bf16 inputs, for gfx950 (MI355X).
 //
-// One workgroup owns one tile of kBr = 128 query rows of one query head and
-// keeps it resident (in registers) while it streams the K/V tiles of the
-// matching K/V head through LDS: the tiling of the reading-notes page
+// One workgroup owns one tile of kBr = 256 query rows of one query head and
+// keeps it resident (in registers, 32 rows per wave) while it streams the
+// K/V tiles of the matching K/V head through LDS: the tiling of the reading-notes page
 // (Methods, step 1: Q stays on chip, K and V are read block by block) in the
 // query-outer loop order the blog names at the end of its blocked derivation
-// (section 带在线Softmax重缩放的分块模式, closing remark).  Per K/V tile:
+// (section 带在线Softmax重缩放的分块模式, closing remark).  Per K/V tile j:
 //
 //   S^T = K_j Q_i^T                 bf16 MFMA 32x32x16, fp32 accumulate
 //   mask (causal / past-the-end)    only on tiles that cross the diagonal or N
@@ -19,6 +19,20 @@
 // u, divide u by l at the end).  The epilogue divides by l and writes the
 // natural-log logsumexp m + ln l that the blog's backward section keeps.
 //
+// One scheduling choice (the arithmetic is that of the method):
+//  * Ping-pong.  The 8 waves form two groups with one wave of each on every
+//    SIMD.  Between workgroup barriers, one group runs a matrix phase
+//    (P_{t-1} V_{t-1} and S_t) while the other runs a vector phase (the
+//    softmax of its S), then they swap, so the matrix cores of each SIMD are
+//    fed by one group while the other keeps the vector ALUs busy.  K tiles
+//    run one tile ahead of V tiles through LDS to fit this order.
+// and one change against a literal reading, exact in real arithmetic:
+//  * Lazy rescaling.  The reference max m of a row only moves when the tile
+//    max exceeds it by more than 2^kLazyLog2 (log2 domain).  Any common
+//    reference value gives the same O = sum p v / sum p and the same
+//    LSE = m + log2 l; the bound keeps every p <= 2^kLazyLog2, far inside
+//    fp32/bf16 range, and skips the O rescale on almost every tile.
+//
 // Layout choices (each checked against the MFMA lane layouts of gfx950):
 //  * Computing S^T rather than S puts one query per lane (column of the
 //    32x32 accumulator), so the row max and row sum are per-lane reductions
@@ -26,11 +40,13 @@
 //  * The S^T accumulator registers 8c..8c+7 of a 32-key block are exactly the
 //    B operand (P^T, 16 keys x 32 queries) of the P V product for the 16-key
 //    chunk c, once the keys of that chunk are taken in the order
-//    {16c+4h+0..3, 16c+8+4h+0..3} for lane half h.  V is read in the same
-//    key order with the LDS transpose read (ds_read_b64_tr_b16), so P never
-//    leaves registers and V keeps its natural [key][d] layout in LDS.
-//  * The O^T accumulator also has one query per lane, so the rescale by
-//    2^(m-m') and the final 1/l are one multiplier per lane.
+//    {16c+4h+0..3, 16c+8+4h+0..3} for lane half h.  V is stored in LDS
+//    transposed (V^T[d][key]) with the keys of each 16-key chunk permuted into
+//    that order, so one 16-byte LDS read per lane gives the V^T operand of an
+//    MFMA and P never leaves registers.  (An LDS read costs a wave about the
+//    same issue time whatever its width, so the wide reads matter.)
+//  * The O^T accumulator also has one query per lane, so the rescale and the
+//    final 1/l are one multiplier per lane.
 #include "fa_kernels.h"
 
 #include <stdint.h>
@@ -43,41 +59,44 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 #define LDS __attribute__((address_space(3)))
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kWaveRows = 32;                    // query rows per wave
 constexpr int kThreads = kWaves * 64;
 constexpr int kBr = kWaves * kWaveRows;          // query rows per workgroup
 static_assert(kBr == kBlockRowsBf16, "grid and kernel disagree on the query tile");
+constexpr float kLazyLog2 = 8.0f;                // max growth tolerated before a rescale
+// s_getreg immediate for HW_REG_HW_ID (id 4), bits [5:4] = SIMD id
+constexpr int kGetregSimdId = 4 | (4 << 6) | ((2 - 1) << 11);
 
-// K/V tile geometry in LDS.  Row pitches are padded so that the MFMA operand
-// reads are free of bank conflicts: K rows are read 16 bytes per lane with
-// consecutive lanes on consecutive keys (pitch = 16 mod 128 bytes); V rows
-// are read 4 rows x 32 bytes per 16 lanes by the transpose read (pitch = 32
-// mod 128 bytes).
+// K/V tile geometry in LDS: two K buffers ([key][d]) and two V^T buffers
+// ([d][permuted key]).  Row pitches are padded so that the 16-byte operand
+// reads, 32 consecutive rows by 32 lanes, are free of bank conflicts (pitch =
+// 16 mod 256 bytes for both).
 template <int D>
 struct Tile {
-    static constexpr int BC = 8192 / D;           // keys per tile: 64 (d=128), 128 (d=64)
+    static constexpr int BC = 64;                 // keys per tile
+    static constexpr int KB = BC / 32;            // 32-key blocks per tile
     static constexpr int KPITCH = 2 * D + 16;
-    static constexpr int VPITCH = 2 * D + 32;
+    static constexpr int VPITCH = 2 * BC + 16;    // V^T row: the tile's keys of one d
     static constexpr int KBYTES = BC * KPITCH;
-    static constexpr int VBYTES = BC * VPITCH;
-    static constexpr int STAGE = KBYTES + VBYTES;
+    static constexpr int VBYTES = D * VPITCH;
+    static constexpr int K0 = 0, K1 = KBYTES, V0 = 2 * KBYTES, V1 = 2 * KBYTES + VBYTES;
+    static constexpr int ROLE = 2 * (KBYTES + VBYTES);      // 16 ints for the wave roles
+    static constexpr int LDS_BYTES = ROLE + 64;
     static constexpr int ROW_CHUNKS = D / 8;       // 16-byte chunks per row
     static constexpr int CHUNKS_PER_THREAD = BC * ROW_CHUNKS / kThreads;
     static_assert(BC * ROW_CHUNKS % kThreads == 0, "tile must split evenly over the threads");
-    static_assert(BC % 32 == 0, "");
 };
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// Sum or max across the two lane halves (lane l and lane l^32 hold the same
-// query): after the swap, out[0] + out[1] is x[l] + x[l^32] in every lane.
+// Lane l and lane l^32 hold the same query: after the swap, out[0] and out[1]
+// are x[l] and x[l^32] in some order, in every lane.
 __device__ __forceinline__ float half_swap_sum(float x) {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
@@ -87,97 +106,277 @@ __device__ __forceinline__ float half_swap_max(float x) {
     return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-// Global -> registers for one K/V tile; rows at or past N read as zero so
-// that masked keys meet finite values.
+// Global -> registers for one K or V tile: a wave-uniform tile base and a
+// 32-bit per-thread offset.  Rows past N are clamped to row N-1: such keys
+// are masked, and V must stay finite under a zero weight.
 template <int D>
-__device__ __forceinline__ void load_kv(const u32x4* __restrict__ kg, const u32x4* __restrict__ vg,
-                                        int key0, int N, int tid,
-                                        u32x4 (&kr)[Tile<D>::CHUNKS_PER_THREAD],
-                                        u32x4 (&vr)[Tile<D>::CHUNKS_PER_THREAD]) {
+__device__ __forceinline__ void load_rows(const u32x4* __restrict__ g, int key0, int N, int tid,
+                                          u32x4 (&r)[Tile<D>::CHUNKS_PER_THREAD]) {
     using T = Tile<D>;
+    const u32x4* gt = g + (size_t)key0 * T::ROW_CHUNKS;
+    if (key0 + T::BC <= N) {
 #pragma unroll
-    for (int c = 0; c < T::CHUNKS_PER_THREAD; ++c) {
-        const int u = c * kThreads + tid;
-        const int row = u / T::ROW_CHUNKS;
-        const int col = u % T::ROW_CHUNKS;
-        const int key = key0 + row;
-        if (key < N) {
-            const size_t off = (size_t)key * T::ROW_CHUNKS + col;
-            kr[c] = kg[off];
-            vr[c] = vg[off];
-        } else {
-            kr[c] = (u32x4){0u, 0u, 0u, 0u};
-            vr[c] = (u32x4){0u, 0u, 0u, 0u};
+        for (int c = 0; c < T::CHUNKS_PER_THREAD; ++c) r[c] = gt[c * kThreads + tid];
+    } else {
+#pragma unroll
+        for (int c = 0; c < T::CHUNKS_PER_THREAD; ++c) {
+            const int u = c * kThreads + tid;
+            const int row = min(u / T::ROW_CHUNKS, N - 1 - key0);
+            r[c] = gt[row * T::ROW_CHUNKS + u % T::ROW_CHUNKS];
         }
     }
 }
 
 template <int D>
-__device__ __forceinline__ void store_kv(LDS char* stage, int tid,
-                                         const u32x4 (&kr)[Tile<D>::CHUNKS_PER_THREAD],
-                                         const u32x4 (&vr)[Tile<D>::CHUNKS_PER_THREAD]) {
+__device__ __forceinline__ void store_k(LDS char* buf, int tid,
+                                        const u32x4 (&r)[Tile<D>::CHUNKS_PER_THREAD]) {
     using T = Tile<D>;
-    LDS char* kl = stage;
-    LDS char* vl = stage + T::KBYTES;
 #pragma unroll
     for (int c = 0; c < T::CHUNKS_PER_THREAD; ++c) {
         const int u = c * kThreads + tid;
-        const int row = u / T::ROW_CHUNKS;
-        const int col = u % T::ROW_CHUNKS;
-        *(LDS u32x4*)(kl + row * T::KPITCH + col * 16) = kr[c];
-        *(LDS u32x4*)(vl + row * T::VPITCH + col * 16) = vr[c];
+        *(LDS u32x4*)(buf + (u / T::ROW_CHUNKS) * T::KPITCH + (u % T::ROW_CHUNKS) * 16) = r[c];
     }
+}
+
+// V loads: one (key pair, 8-wide d chunk) per thread, j = tid % 32 and
+// c8 = tid / 32: rows 2j and 2j+1 of chunk c8 (threads past the tile's pair
+// count, for d = 64, load nothing).
+template <int D>
+struct VMap {
+    static constexpr int THREADS = (Tile<D>::BC / 2) * (D / 8);
+    static_assert(THREADS <= kThreads && THREADS % 64 == 0, "");
+};
+
+template <int D>
+__device__ __forceinline__ void load_v(const u32x4* __restrict__ g, int key0, int N, int tid,
+                                       u32x4 (&r)[2]) {
+    using T = Tile<D>;
+    if (tid >= VMap<D>::THREADS) return;
+    const u32x4* gt = g + (size_t)key0 * T::ROW_CHUNKS;
+    const int j = tid & 31;
+    const int c8 = tid >> 5;
+    const int last = N - 1 - key0;             // last valid row of the tile
+    r[0] = gt[min(2 * j, last) * T::ROW_CHUNKS + c8];
+    r[1] = gt[min(2 * j + 1, last) * T::ROW_CHUNKS + c8];
+}
+
+// Permuted position of key k (0..BC-1) inside a V^T row: within each 16-key
+// chunk, key 8*b3 + 4*b2 + b moves to 8*b2 + 4*b3 + b.
+__device__ __forceinline__ int vt_pos(int k) {
+    return (k & ~15) | ((k & 4) << 1) | ((k & 8) >> 1) | (k & 3);
+}
+
+template <int D>
+__device__ __forceinline__ void store_vt(LDS char* buf, int tid, const u32x4 (&r)[2]) {
+    using T = Tile<D>;
+    if (tid >= VMap<D>::THREADS) return;
+    const int j = tid & 31;
+    const int c8 = tid >> 5;
+    LDS char* dst = buf + 8 * c8 * T::VPITCH + vt_pos(2 * j) * 2;   // keys 2j, 2j+1 stay adjacent
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        // d = 8*c8 + 2e and 2e+1: pack (V[2j][d], V[2j+1][d]) for each d
+        const uint32_t a = __builtin_amdgcn_perm(r[1][e], r[0][e], 0x05040100u);
+        const uint32_t b = __builtin_amdgcn_perm(r[1][e], r[0][e], 0x07060302u);
+        *(LDS uint32_t*)(dst + (2 * e) * T::VPITCH) = a;
+        *(LDS uint32_t*)(dst + (2 * e + 1) * T::VPITCH) = b;
+    }
+}
+
+// The matrix phase of one tile step: O^T += V^T P^T for the previous tile
+// (HAS_PV) and S^T = K Q^T for the current one (HAS_S), as one stream of
+// 16-byte LDS operand reads and MFMAs.  The reads run kAhead MFMAs ahead of
+// their use (scheduling groups below), so the LDS latency stays hidden
+// behind the matrix core instead of stalling every MFMA.
+constexpr int kAhead = 4;
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
+
+template <int D, bool HAS_PV, bool HAS_S>
+__device__ __forceinline__ void gemm_phase(const LDS char* vl, const LDS char* kl,
+                                           const bf16x8 (&pb)[Tile<D>::BC / 16],
+                                           const bf16x8 (&qf)[D / 16], f32x16 (&oacc)[D / 32],
+                                           f32x16 (&s)[Tile<D>::KB], int lane) {
+    using T = Tile<D>;
+    constexpr int DB = D / 32;
+    constexpr int NPV = HAS_PV ? (T::BC / 16) * DB : 0;
+    constexpr int NS = HAS_S ? (D / 16) * T::KB : 0;
+    constexpr int NF = NPV + NS;
+    const int h = lane >> 5;
+    const int l32 = lane & 31;
+    const LDS char* vrow = vl + l32 * T::VPITCH + 16 * h;
+    const LDS char* krow = kl + l32 * T::KPITCH + 16 * h;
+    bf16x8 fr[NF > 0 ? NF : 1];
+#pragma unroll
+    for (int i = 0; i < NF; ++i) {
+        if (i < NPV) {
+            const int cc = i / DB, db = i % DB;
+            fr[i] = *(const LDS bf16x8*)(vrow + 32 * db * T::VPITCH + 32 * cc);
+        } else {
+            const int ks = (i - NPV) / T::KB, kb = (i - NPV) % T::KB;
+            fr[i] = *(const LDS bf16x8*)(krow + 32 * kb * T::KPITCH + 32 * ks);
+        }
+    }
+    if constexpr (HAS_S) {
+#pragma unroll
+        for (int kb = 0; kb < T::KB; ++kb) s[kb] = (f32x16){};
+    }
+#pragma unroll
+    for (int i = 0; i < NF; ++i) {
+        if (i < NPV) {
+            const int cc = i / DB, db = i % DB;
+            oacc[db] = mfma32(fr[i], pb[cc], oacc[db]);
+        } else {
+            const int ks = (i - NPV) / T::KB, kb = (i - NPV) % T::KB;
+            s[kb] = mfma32(fr[i], qf[ks], s[kb]);
+        }
+    }
+    if constexpr (NF > kAhead) {
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kAhead, 0);
+#pragma unroll
+        for (int i = 0; i < NF - kAhead; ++i) {
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, kAhead, 0);
+    }
+}
+
+// Online softmax of one tile of S^T: mask, row max, lazy rescale of the
+// running state, P = exp2(S*c - m) in bf16 for the P V product, row sum.
+template <int D, bool CAUSAL, bool MASK>
+__device__ __forceinline__ void softmax_tile(f32x16 (&s)[Tile<D>::KB], bf16x8 (&pb)[Tile<D>::BC / 16],
+                                             f32x16 (&oacc)[D / 32], float& m_run, float& l_run,
+                                             int key0, int N, int my_row, float c_log2, int lane) {
+    using T = Tile<D>;
+    constexpr int KB = T::KB;
+    const int h = lane >> 5;
+
+    if constexpr (MASK) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int key = key0 + 32 * kb + 8 * (i >> 2) + 4 * h + (i & 3);
+                const bool dead = key >= N || (CAUSAL && key > my_row);
+                if (dead) s[kb][i] = -__builtin_inff();
+            }
+        }
+    }
+
+    // row max: a tree over the lane's 32 values, then the other half's
+    float mx[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) mx[t] = fmaxf(fmaxf(s[0][4 * t], s[0][4 * t + 1]), fmaxf(s[0][4 * t + 2], s[0][4 * t + 3]));
+#pragma unroll
+    for (int kb = 1; kb < KB; ++kb)
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+            mx[t] = fmaxf(fmaxf(mx[t], s[kb][4 * t]), fmaxf(fmaxf(s[kb][4 * t + 1], s[kb][4 * t + 2]), s[kb][4 * t + 3]));
+    const float tile_max = half_swap_max(fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3])));
+
+    const float cand = tile_max * c_log2;
+    const bool grow = cand > m_run + kLazyLog2;      // false while cand is -inf
+    const float m_new = grow ? cand : m_run;
+    const float m_use = (m_new == -__builtin_inff()) ? 0.f : m_new;
+    // rescale (rare): only when some row of the wave moved its reference max
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);   // 1 where the max stayed
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
+    }
+    m_run = m_new;
+
+    float ps[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][i], c_log2, -m_use));
+            ps[i & 3] += p;
+            pb[2 * kb + (i >> 3)][i & 7] = (__bf16)p;
+        }
+    l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
 }
 
 // c_log2 = |scale| * log2(e) (> 0); qsign flips the sign bit of every Q
 // element when scale < 0 (exact), so that the kernel only sees c_log2 > 0.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
+__global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     __bf16* __restrict__ O, float* __restrict__ LSE, int group, int N, int n_qtiles, int bh_total,
     float c_log2, uint32_t qsign) {
     using T = Tile<D>;
     constexpr int BC = T::BC;
-    constexpr int KB = BC / 32;        // 32-key blocks per tile
-    constexpr int DB = D / 32;         // 32-wide d blocks of the output
-    constexpr int KSTEPS = D / 16;     // contraction steps of S
+    constexpr int KB = T::KB;
+    constexpr int DB = D / 32;
+    constexpr int KSTEPS = D / 16;
 
-    __shared__ __attribute__((aligned(16))) char smem_raw[2 * T::STAGE];
+    __shared__ __attribute__((aligned(16))) char smem_raw[T::LDS_BYTES];
     LDS char* smem = (LDS char*)smem_raw;
+    LDS int* roles = (LDS int*)(smem + T::ROLE);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int h = lane >> 5;           // lane half
+    const int h = lane >> 5;
     const int l32 = lane & 31;
 
     // Work decomposition.  Workgroups are dealt round-robin to the 8 XCDs
     // (w % 8); give each XCD a contiguous range of heads so that the query
-    // tiles sharing one K/V head (and a GQA group) share that XCD's L2.
-    // Causal tiles run heaviest (latest) first.
+    // tiles sharing one K/V head (and a GQA group) share that XCD's L2 and
+    // MALL slice.  Within an XCD, query tiles go out in rounds over its heads,
+    // latest (heaviest, when causal) tiles first, so the short tiles fill the
+    // tail of the launch.
     int bh, qt;
     {
         const int w = blockIdx.x;
         if ((bh_total & 7) == 0) {
             const int slot = w >> 3;
-            bh = (w & 7) * (bh_total >> 3) + slot / n_qtiles;
-            qt = slot % n_qtiles;
+            bh = (w & 7) * (bh_total >> 3) + slot % (bh_total >> 3);
+            qt = slot / (bh_total >> 3);
         } else {
             bh = w / n_qtiles;
             qt = w % n_qtiles;
         }
         if (CAUSAL) qt = n_qtiles - 1 - qt;
     }
+
+    // Wave roles.  Order the waves by (rank among the waves on the same SIMD,
+    // SIMD id, wave id): the first four form the group that starts with a
+    // matrix phase, the last four the group that starts one phase later, so
+    // that each SIMD gets one wave of each group.  The order is a permutation
+    // of the 8 waves whatever the placement, so the row blocks stay a
+    // partition of the tile.
+    int grp, idx;
+    {
+        const int simd = __builtin_amdgcn_s_getreg(kGetregSimdId) & 3;
+        if (lane == 0) roles[wave] = simd;
+        __syncthreads();
+        int rank = 0;
+        for (int v = 0; v < wave; ++v) rank += roles[v] == simd;
+        const int key = (rank * 4 + simd) * kWaves + wave;
+        __syncthreads();
+        if (lane == 0) roles[8 + wave] = key;
+        __syncthreads();
+        int pos = 0;
+        for (int v = 0; v < kWaves; ++v) pos += roles[8 + v] < key;
+        grp = pos >> 2;
+        idx = pos & 3;
+    }
+    const int rblock = 2 * idx + grp;         // the groups interleave 32-row blocks
+
     const size_t q_head = (size_t)bh * N * D;
     const size_t kv_head = (size_t)(bh / group) * N * D;
     const int q0 = qt * kBr;
-    const int wq0 = q0 + wave * kWaveRows;    // first query row of this wave
+    const int wq0 = q0 + rblock * kWaveRows;  // first query row of this wave
     const int my_row = wq0 + l32;             // the query row this lane owns
 
     // Q fragments: B operand of S^T = K Q^T, lane holds d = 16*ks + 8*h .. +7.
     bf16x8 qf[KSTEPS];
     {
-        const u32x4* qp = (const u32x4*)(Q + q_head + (size_t)(my_row < N ? my_row : N - 1) * D);
+        const u32x4* qp = (const u32x4*)(Q + q_head + (size_t)min(my_row, N - 1) * D);
 #pragma unroll
         for (int ks = 0; ks < KSTEPS; ++ks) {
             u32x4 x = qp[2 * ks + h];
@@ -198,95 +397,68 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     f32x16 oacc[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db) oacc[db] = (f32x16){};
-    float m_run = -__builtin_inff();   // running max of S*c (log2 domain)
+    float m_run = -__builtin_inff();   // reference max of S*c (log2 domain)
     float l_run = 0.f;                 // this lane's share of the running sum
+    f32x16 s[KB];
+    bf16x8 pb[BC / 16];
 
-    u32x4 kr[T::CHUNKS_PER_THREAD], vr[T::CHUNKS_PER_THREAD];
-    load_kv<D>(kg, vg, 0, N, tid, kr, vr);
-    store_kv<D>(smem, tid, kr, vr);
+    // Global loads run four phases ahead of their LDS stores: load group u =
+    // (K_{u+1}, V_u) is fetched in phase 2u-2 into register set u&1 and
+    // written to LDS at the end of phase 2u+1.
+    u32x4 kr0[T::CHUNKS_PER_THREAD], kr1[T::CHUNKS_PER_THREAD], vr0[2], vr1[2];
+    load_rows<D>(kg, 0, N, tid, kr0);
+    store_k<D>(smem + T::K0, tid, kr0);
+    if (1 < n_tiles) load_rows<D>(kg, BC, N, tid, kr0);
+    load_v<D>(vg, 0, N, tid, vr0);
     __syncthreads();
 
-    // lane-constant parts of the V transpose-read address
-    const int v_row_lane = 4 * h + ((lane & 15) >> 2);
-    const int v_col_lane = 2 * (16 * ((lane >> 4) & 1) + 4 * (lane & 3));
-
-    for (int j = 0; j < n_tiles; ++j) {
-        const bool more = j + 1 < n_tiles;
-        if (more) load_kv<D>(kg, vg, (j + 1) * BC, N, tid, kr, vr);
-
-        if (j < w_tiles) {
-            LDS char* kl = smem + (j & 1) * T::STAGE;
-            LDS char* vl = kl + T::KBYTES;
-
-            f32x16 s[KB];
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) s[kb] = (f32x16){};
-#pragma unroll
-            for (int ks = 0; ks < KSTEPS; ++ks) {
-#pragma unroll
-                for (int kb = 0; kb < KB; ++kb) {
-                    const bf16x8 a = *(LDS bf16x8*)(kl + (32 * kb + l32) * T::KPITCH + (16 * ks + 8 * h) * 2);
-                    s[kb] = mfma32(a, qf[ks], s[kb]);
-                }
-            }
-
-            // Accumulator register 4g+r of block kb holds key 32kb + 8g + 4h + r.
-            const int key0 = j * BC;
-            const bool need_mask = (key0 + BC > N) || (CAUSAL && key0 + BC - 1 > wq0);
-            if (need_mask) {
-#pragma unroll
-                for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int key = key0 + 32 * kb + 8 * (i >> 2) + 4 * h + (i & 3);
-                        const bool dead = key >= N || (CAUSAL && key > my_row);
-                        if (dead) s[kb][i] = -__builtin_inff();
-                    }
-                }
-            }
-
-            float mx = s[0][0];
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-            mx = half_swap_max(mx);
-            const float m_new = fmaxf(m_run, mx * c_log2);
-            const float m_use = (m_new == -__builtin_inff()) ? 0.f : m_new;
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-
-            float psum = 0.f;
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][i], c_log2, -m_use));
-                    s[kb][i] = p;
-                    psum += p;
-                }
-            l_run = fmaf(l_run, alpha, psum);
-            m_run = m_new;
-#pragma unroll
-            for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
-
-#pragma unroll
-            for (int cc = 0; cc < BC / 16; ++cc) {
-                bf16x8 pb;
-#pragma unroll
-                for (int t = 0; t < 8; ++t) pb[t] = (__bf16)s[cc >> 1][8 * (cc & 1) + t];
-                LDS char* vrow = vl + (16 * cc + v_row_lane) * T::VPITCH + v_col_lane;
-#pragma unroll
-                for (int db = 0; db < DB; ++db) {
-                    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS i16x4*)(vrow + 64 * db));
-                    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS i16x4*)(vrow + 8 * T::VPITCH + 64 * db));
-                    const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-                    oacc[db] = mfma32(a, pb, oacc[db]);
-                }
-            }
+    // Phases p = 0 .. 2*n_tiles+1, each closed by a workgroup barrier.  The
+    // group's local phase lp = p - grp: even lp = 2t is the matrix phase t
+    // (P_{t-1} V_{t-1}, then S_t), odd lp = 2t+1 the softmax of S_t.  K_t is
+    // read in phases 2t (first group) and 2t+1 (second); V_t in 2t+2 and
+    // 2t+3.  K_{t+1} and V_t are written to LDS at the end of phase 2t+1,
+    // into the buffers of K_{t-1} and V_{t-2}, whose last readers finished in
+    // phase 2t-1.
+    auto phase = [&](int p) __attribute__((always_inline)) {
+        const int lp = p - grp;
+        if (lp < 0) return;
+        const int t = lp >> 1;
+        if ((lp & 1) == 0) {
+            const bool has_pv = t >= 1 && t - 1 < w_tiles;
+            const bool has_s = t < w_tiles;
+            const LDS char* vl = smem + ((t - 1) & 1 ? T::V1 : T::V0);
+            const LDS char* kl = smem + (t & 1 ? T::K1 : T::K0);
+            if (has_pv && has_s)
+                gemm_phase<D, true, true>(vl, kl, pb, qf, oacc, s, lane);
+            else if (has_pv)
+                gemm_phase<D, true, false>(vl, kl, pb, qf, oacc, s, lane);
+            else if (has_s)
+                gemm_phase<D, false, true>(vl, kl, pb, qf, oacc, s, lane);
+        } else if (t < w_tiles) {
+            const int key0 = t * BC;
+            if ((key0 + BC > N) || (CAUSAL && key0 + BC - 1 > wq0))
+                softmax_tile<D, CAUSAL, true>(s, pb, oacc, m_run, l_run, key0, N, my_row, c_log2, lane);
+            else
+                softmax_tile<D, CAUSAL, false>(s, pb, oacc, m_run, l_run, key0, N, my_row, c_log2, lane);
         }
-
-        if (more) store_kv<D>(smem + ((j + 1) & 1) * T::STAGE, tid, kr, vr);
+    };
+    // one tile step: phases 2u and 2u+1, issuing group u+1 into (kn, vn) and
+    // storing group u from (kc, vc)
+    auto tile_pair = [&](int u, u32x4 (&kc)[T::CHUNKS_PER_THREAD], u32x4 (&vc)[2],
+                         u32x4 (&kn)[T::CHUNKS_PER_THREAD], u32x4 (&vn)[2]) __attribute__((always_inline)) {
+        if (u + 2 < n_tiles) load_rows<D>(kg, (u + 2) * BC, N, tid, kn);
+        if (u + 1 < n_tiles) load_v<D>(vg, (u + 1) * BC, N, tid, vn);
+        phase(2 * u);
         __syncthreads();
+        phase(2 * u + 1);
+        if (u + 1 < n_tiles) store_k<D>(smem + ((u + 1) & 1 ? T::K1 : T::K0), tid, kc);
+        if (u < n_tiles) store_vt<D>(smem + (u & 1 ? T::V1 : T::V0), tid, vc);
+        __syncthreads();
+    };
+#pragma unroll 1
+    for (int u = 0; u <= n_tiles; u += 2) {
+        tile_pair(u, kr0, vr0, kr1, vr1);
+        if (u + 1 <= n_tiles) tile_pair(u + 1, kr1, vr1, kr0, vr0);
     }
 
     if (wq0 >= N) return;

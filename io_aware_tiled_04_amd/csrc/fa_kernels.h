@@ -21,7 +21,7 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
 
 // Query rows per workgroup of the bf16 kernel (the grid is B*Hq*ceil(N/kBlockRowsBf16)).
-constexpr int kBlockRowsBf16 = 128;
+constexpr int kBlockRowsBf16 = 256;
 // Query rows per workgroup of the fp32 kernel.
 constexpr int kBlockRowsF32 = 64;
 
