@@ -108,22 +108,20 @@ __device__ __forceinline__ float half_swap_max(float x) {
 
 // Global -> registers for one K or V tile: a wave-uniform tile base and a
 // 32-bit per-thread offset.  Rows past N are clamped to row N-1: such keys
-// are masked, and V must stay finite under a zero weight.
+// are masked, and V must stay finite under a zero weight.  The loads are
+// branch-free and every call issues the same number of them, so that the
+// wait before their LDS store can count only the loads issued before them.
 template <int D>
 __device__ __forceinline__ void load_rows(const u32x4* __restrict__ g, int key0, int N, int tid,
                                           u32x4 (&r)[Tile<D>::CHUNKS_PER_THREAD]) {
     using T = Tile<D>;
     const u32x4* gt = g + (size_t)key0 * T::ROW_CHUNKS;
-    if (key0 + T::BC <= N) {
+    const int last = N - 1 - key0;             // last valid row of the tile
 #pragma unroll
-        for (int c = 0; c < T::CHUNKS_PER_THREAD; ++c) r[c] = gt[c * kThreads + tid];
-    } else {
-#pragma unroll
-        for (int c = 0; c < T::CHUNKS_PER_THREAD; ++c) {
-            const int u = c * kThreads + tid;
-            const int row = min(u / T::ROW_CHUNKS, N - 1 - key0);
-            r[c] = gt[row * T::ROW_CHUNKS + u % T::ROW_CHUNKS];
-        }
+    for (int c = 0; c < T::CHUNKS_PER_THREAD; ++c) {
+        const int u = c * kThreads + tid;
+        const int row = min(u / T::ROW_CHUNKS, last);
+        r[c] = gt[row * T::ROW_CHUNKS + u % T::ROW_CHUNKS];
     }
 }
 
@@ -139,8 +137,8 @@ __device__ __forceinline__ void store_k(LDS char* buf, int tid,
 }
 
 // V loads: one (key pair, 8-wide d chunk) per thread, j = tid % 32 and
-// c8 = tid / 32: rows 2j and 2j+1 of chunk c8 (threads past the tile's pair
-// count, for d = 64, load nothing).
+// c8 = tid / 32: rows 2j and 2j+1 of chunk c8.  Threads past the tile's pair
+// count (for d = 64) load a duplicate that they do not store.
 template <int D>
 struct VMap {
     static constexpr int THREADS = (Tile<D>::BC / 2) * (D / 8);
@@ -151,10 +149,9 @@ template <int D>
 __device__ __forceinline__ void load_v(const u32x4* __restrict__ g, int key0, int N, int tid,
                                        u32x4 (&r)[2]) {
     using T = Tile<D>;
-    if (tid >= VMap<D>::THREADS) return;
     const u32x4* gt = g + (size_t)key0 * T::ROW_CHUNKS;
     const int j = tid & 31;
-    const int c8 = tid >> 5;
+    const int c8 = (tid >> 5) % (D / 8);
     const int last = N - 1 - key0;             // last valid row of the tile
     r[0] = gt[min(2 * j, last) * T::ROW_CHUNKS + c8];
     r[1] = gt[min(2 * j + 1, last) * T::ROW_CHUNKS + c8];
@@ -404,11 +401,13 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
 
     // Global loads run four phases ahead of their LDS stores: load group u =
     // (K_{u+1}, V_u) is fetched in phase 2u-2 into register set u&1 and
-    // written to LDS at the end of phase 2u+1.
+    // written to LDS at the end of phase 2u+1.  Past the last tile the loads
+    // repeat the last tile (in bounds, never stored), so every step issues
+    // the same loads.
     u32x4 kr0[T::CHUNKS_PER_THREAD], kr1[T::CHUNKS_PER_THREAD], vr0[2], vr1[2];
     load_rows<D>(kg, 0, N, tid, kr0);
     store_k<D>(smem + T::K0, tid, kr0);
-    if (1 < n_tiles) load_rows<D>(kg, BC, N, tid, kr0);
+    load_rows<D>(kg, min(1, n_tiles - 1) * BC, N, tid, kr0);
     load_v<D>(vg, 0, N, tid, vr0);
     __syncthreads();
 
@@ -446,8 +445,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     // storing group u from (kc, vc)
     auto tile_pair = [&](int u, u32x4 (&kc)[T::CHUNKS_PER_THREAD], u32x4 (&vc)[2],
                          u32x4 (&kn)[T::CHUNKS_PER_THREAD], u32x4 (&vn)[2]) __attribute__((always_inline)) {
-        if (u + 2 < n_tiles) load_rows<D>(kg, (u + 2) * BC, N, tid, kn);
-        if (u + 1 < n_tiles) load_v<D>(vg, (u + 1) * BC, N, tid, vn);
+        load_rows<D>(kg, min(u + 2, n_tiles - 1) * BC, N, tid, kn);
+        load_v<D>(vg, min(u + 1, n_tiles - 1) * BC, N, tid, vn);
         phase(2 * u);
         __syncthreads();
         phase(2 * u + 1);
