@@ -19,19 +19,27 @@
 // u, divide u by l at the end).  The epilogue divides by l and writes the
 // natural-log logsumexp m + ln l that the blog's backward section keeps.
 //
-// One scheduling choice (the arithmetic is that of the method):
+// Scheduling choices (the arithmetic is that of the method):
 //  * Ping-pong.  The 8 waves form two groups with one wave of each on every
 //    SIMD.  Between workgroup barriers, one group runs a matrix phase
 //    (P_{t-1} V_{t-1} and S_t) while the other runs a vector phase (the
 //    softmax of its S), then they swap, so the matrix cores of each SIMD are
 //    fed by one group while the other keeps the vector ALUs busy.  K tiles
-//    run one tile ahead of V tiles through LDS to fit this order.
+//    run one tile ahead of V tiles through LDS to fit this order.  A wave
+//    raises its issue priority for its matrix phase.
+//  * Copies by the vector phase.  The matrix phase reads one 16-byte LDS
+//    operand per MFMA, about as fast as one wave can read LDS, so every
+//    other LDS access in that phase slows it.  The second group therefore
+//    copies K tiles and the first group V tiles, each writing to LDS only in
+//    its own vector phase.
 // and one change against a literal reading, exact in real arithmetic:
-//  * Lazy rescaling.  The reference max m of a row only moves when the tile
-//    max exceeds it by more than 2^kLazyLog2 (log2 domain).  Any common
-//    reference value gives the same O = sum p v / sum p and the same
-//    LSE = m + log2 l; the bound keeps every p <= 2^kLazyLog2, far inside
-//    fp32/bf16 range, and skips the O rescale on almost every tile.
+//  * Lazy rescaling.  The reference max m of a row is the exact row max of
+//    the first tile; afterwards P is taken against it directly, and m only
+//    moves (to the exact max, with a rescale of O and l and a redo of the
+//    tile) when a row sum of the tile exceeds kSumLimit = 2^20, i.e. before
+//    any p can leave [0, 2^20].  Any common reference value gives the same
+//    O = sum p v / sum p and the same LSE = m + log2 l, and almost every
+//    tile skips both the row max and the rescale.
 //
 // Layout choices (each checked against the MFMA lane layouts of gfx950):
 //  * Computing S^T rather than S puts one query per lane (column of the
@@ -66,8 +74,10 @@ constexpr int kWaves = 8;
 constexpr int kWaveRows = 32;                    // query rows per wave
 constexpr int kThreads = kWaves * 64;
 constexpr int kBr = kWaves * kWaveRows;          // query rows per workgroup
+constexpr int kGroupThreads = kThreads / 2;      // threads of one wave group
 static_assert(kBr == kBlockRowsBf16, "grid and kernel disagree on the query tile");
-constexpr float kLazyLog2 = 8.0f;                // max growth tolerated before a rescale
+constexpr float kSumLimit = 1048576.0f;          // 2^20: largest row sum of a tile before a rescale
+constexpr int kMatrixPrio = 3;                   // wave issue priority during a matrix phase
 // s_getreg immediate for HW_REG_HW_ID (id 4), bits [5:4] = SIMD id
 constexpr int kGetregSimdId = 4 | (4 << 6) | ((2 - 1) << 11);
 
@@ -87,8 +97,15 @@ struct Tile {
     static constexpr int ROLE = 2 * (KBYTES + VBYTES);      // 16 ints for the wave roles
     static constexpr int LDS_BYTES = ROLE + 64;
     static constexpr int ROW_CHUNKS = D / 8;       // 16-byte chunks per row
-    static constexpr int CHUNKS_PER_THREAD = BC * ROW_CHUNKS / kThreads;
-    static_assert(BC * ROW_CHUNKS % kThreads == 0, "tile must split evenly over the threads");
+    // One wave group (kGroupThreads threads) copies a whole K or V tile:
+    // K as 16-byte row chunks, V as (key pair, 8-wide d chunk) items of two
+    // 16-byte loads; both come to STAGE 16-byte registers per thread.
+    static constexpr int K_CHUNKS = BC * ROW_CHUNKS / kGroupThreads;
+    static constexpr int V_ITEMS = (BC / 2) * (D / 8) / kGroupThreads;
+    static constexpr int STAGE = K_CHUNKS;
+    static_assert(BC * ROW_CHUNKS % kGroupThreads == 0 && (BC / 2) * (D / 8) % kGroupThreads == 0,
+                  "tiles must split evenly over a wave group");
+    static_assert(2 * V_ITEMS == K_CHUNKS, "K and V copies use the same staging registers");
 };
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -106,55 +123,50 @@ __device__ __forceinline__ float half_swap_max(float x) {
     return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-// Global -> registers for one K or V tile: a wave-uniform tile base and a
-// 32-bit per-thread offset.  Rows past N are clamped to row N-1: such keys
-// are masked, and V must stay finite under a zero weight.  The loads are
+// K/V copies (global -> registers -> LDS) by one wave group; gt is the
+// thread's index in its group.  Rows past N are clamped to row N-1: such
+// keys are masked, and V must stay finite under a zero weight.  The loads are
 // branch-free and every call issues the same number of them, so that the
-// wait before their LDS store can count only the loads issued before them.
+// wait before an LDS store counts only the loads issued before its own.
 template <int D>
-__device__ __forceinline__ void load_rows(const u32x4* __restrict__ g, int key0, int N, int tid,
-                                          u32x4 (&r)[Tile<D>::CHUNKS_PER_THREAD]) {
+using Stage = u32x4[Tile<D>::STAGE];
+
+template <int D>
+__device__ __forceinline__ void load_k(const u32x4* __restrict__ g, int key0, int N, int gt, Stage<D>& r) {
     using T = Tile<D>;
-    const u32x4* gt = g + (size_t)key0 * T::ROW_CHUNKS;
+    const u32x4* gtile = g + (size_t)key0 * T::ROW_CHUNKS;
     const int last = N - 1 - key0;             // last valid row of the tile
 #pragma unroll
-    for (int c = 0; c < T::CHUNKS_PER_THREAD; ++c) {
-        const int u = c * kThreads + tid;
-        const int row = min(u / T::ROW_CHUNKS, last);
-        r[c] = gt[row * T::ROW_CHUNKS + u % T::ROW_CHUNKS];
+    for (int c = 0; c < T::K_CHUNKS; ++c) {
+        const int u = c * kGroupThreads + gt;
+        r[c] = gtile[min(u / T::ROW_CHUNKS, last) * T::ROW_CHUNKS + u % T::ROW_CHUNKS];
     }
 }
 
 template <int D>
-__device__ __forceinline__ void store_k(LDS char* buf, int tid,
-                                        const u32x4 (&r)[Tile<D>::CHUNKS_PER_THREAD]) {
+__device__ __forceinline__ void store_k(LDS char* buf, int gt, const Stage<D>& r) {
     using T = Tile<D>;
 #pragma unroll
-    for (int c = 0; c < T::CHUNKS_PER_THREAD; ++c) {
-        const int u = c * kThreads + tid;
+    for (int c = 0; c < T::K_CHUNKS; ++c) {
+        const int u = c * kGroupThreads + gt;
         *(LDS u32x4*)(buf + (u / T::ROW_CHUNKS) * T::KPITCH + (u % T::ROW_CHUNKS) * 16) = r[c];
     }
 }
 
-// V loads: one (key pair, 8-wide d chunk) per thread, j = tid % 32 and
-// c8 = tid / 32: rows 2j and 2j+1 of chunk c8.  Threads past the tile's pair
-// count (for d = 64) load a duplicate that they do not store.
+// V items: u = c * kGroupThreads + gt is (key pair j = u % 32, d chunk
+// c8 = u / 32): rows 2j and 2j+1 of that chunk, into r[2c] and r[2c+1].
 template <int D>
-struct VMap {
-    static constexpr int THREADS = (Tile<D>::BC / 2) * (D / 8);
-    static_assert(THREADS <= kThreads && THREADS % 64 == 0, "");
-};
-
-template <int D>
-__device__ __forceinline__ void load_v(const u32x4* __restrict__ g, int key0, int N, int tid,
-                                       u32x4 (&r)[2]) {
+__device__ __forceinline__ void load_v(const u32x4* __restrict__ g, int key0, int N, int gt, Stage<D>& r) {
     using T = Tile<D>;
-    const u32x4* gt = g + (size_t)key0 * T::ROW_CHUNKS;
-    const int j = tid & 31;
-    const int c8 = (tid >> 5) % (D / 8);
-    const int last = N - 1 - key0;             // last valid row of the tile
-    r[0] = gt[min(2 * j, last) * T::ROW_CHUNKS + c8];
-    r[1] = gt[min(2 * j + 1, last) * T::ROW_CHUNKS + c8];
+    const u32x4* gtile = g + (size_t)key0 * T::ROW_CHUNKS;
+    const int last = N - 1 - key0;
+#pragma unroll
+    for (int c = 0; c < T::V_ITEMS; ++c) {
+        const int u = c * kGroupThreads + gt;
+        const int j = u & 31, c8 = u >> 5;
+        r[2 * c] = gtile[min(2 * j, last) * T::ROW_CHUNKS + c8];
+        r[2 * c + 1] = gtile[min(2 * j + 1, last) * T::ROW_CHUNKS + c8];
+    }
 }
 
 // Permuted position of key k (0..BC-1) inside a V^T row: within each 16-key
@@ -164,19 +176,21 @@ __device__ __forceinline__ int vt_pos(int k) {
 }
 
 template <int D>
-__device__ __forceinline__ void store_vt(LDS char* buf, int tid, const u32x4 (&r)[2]) {
+__device__ __forceinline__ void store_vt(LDS char* buf, int gt, const Stage<D>& r) {
     using T = Tile<D>;
-    if (tid >= VMap<D>::THREADS) return;
-    const int j = tid & 31;
-    const int c8 = tid >> 5;
-    LDS char* dst = buf + 8 * c8 * T::VPITCH + vt_pos(2 * j) * 2;   // keys 2j, 2j+1 stay adjacent
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        // d = 8*c8 + 2e and 2e+1: pack (V[2j][d], V[2j+1][d]) for each d
-        const uint32_t a = __builtin_amdgcn_perm(r[1][e], r[0][e], 0x05040100u);
-        const uint32_t b = __builtin_amdgcn_perm(r[1][e], r[0][e], 0x07060302u);
-        *(LDS uint32_t*)(dst + (2 * e) * T::VPITCH) = a;
-        *(LDS uint32_t*)(dst + (2 * e + 1) * T::VPITCH) = b;
+    for (int c = 0; c < T::V_ITEMS; ++c) {
+        const int u = c * kGroupThreads + gt;
+        const int j = u & 31, c8 = u >> 5;
+        LDS char* dst = buf + 8 * c8 * T::VPITCH + vt_pos(2 * j) * 2;   // keys 2j, 2j+1 stay adjacent
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            // d = 8*c8 + 2e and 2e+1: pack (V[2j][d], V[2j+1][d]) for each d
+            const uint32_t a = __builtin_amdgcn_perm(r[2 * c + 1][e], r[2 * c][e], 0x05040100u);
+            const uint32_t b = __builtin_amdgcn_perm(r[2 * c + 1][e], r[2 * c][e], 0x07060302u);
+            *(LDS uint32_t*)(dst + (2 * e) * T::VPITCH) = a;
+            *(LDS uint32_t*)(dst + (2 * e + 1) * T::VPITCH) = b;
+        }
     }
 }
 
@@ -239,12 +253,34 @@ __device__ __forceinline__ void gemm_phase(const LDS char* vl, const LDS char* k
     }
 }
 
-// Online softmax of one tile of S^T: mask, row max, lazy rescale of the
-// running state, P = exp2(S*c - m) in bf16 for the P V product, row sum.
+// P = exp2(S*c - m) of one tile in bf16 for the P V product; returns this
+// lane's share of the row sum (over the fp32 values).
+template <int D>
+__device__ __forceinline__ float exp_tile(const f32x16 (&s)[Tile<D>::KB], bf16x8 (&pb)[Tile<D>::BC / 16],
+                                          float m_use, float c_log2) {
+    float ps[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < Tile<D>::KB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][i], c_log2, -m_use));
+            ps[i & 3] += p;
+            pb[2 * kb + (i >> 3)][i & 7] = (__bf16)p;
+        }
+    return (ps[0] + ps[1]) + (ps[2] + ps[3]);
+}
+
+// Online softmax of one tile of S^T: mask, P against the reference max m,
+// row sum.  The reference max is lazy: after the first tile it only moves
+// when some p of the wave would exceed kSumLimit (detected through the row
+// sums, which also catch an overflow to inf); then the tile is redone
+// against its exact row max, after rescaling O and l.  Any common
+// reference gives the same O = sum p v / sum p and LSE = m + log2 l.
 template <int D, bool CAUSAL, bool MASK>
 __device__ __forceinline__ void softmax_tile(f32x16 (&s)[Tile<D>::KB], bf16x8 (&pb)[Tile<D>::BC / 16],
                                              f32x16 (&oacc)[D / 32], float& m_run, float& l_run,
-                                             int key0, int N, int my_row, float c_log2, int lane) {
+                                             int key0, int N, int my_row, float c_log2, int lane,
+                                             bool first) {
     using T = Tile<D>;
     constexpr int KB = T::KB;
     const int h = lane >> 5;
@@ -261,7 +297,15 @@ __device__ __forceinline__ void softmax_tile(f32x16 (&s)[Tile<D>::KB], bf16x8 (&
         }
     }
 
-    // row max: a tree over the lane's 32 values, then the other half's
+    if (!first) {
+        const float ps = exp_tile<D>(s, pb, m_run, c_log2);
+        if (__builtin_amdgcn_ballot_w64(!(ps <= kSumLimit)) == 0) {
+            l_run += ps;
+            return;
+        }
+    }
+
+    // exact row max: a tree over the lane's 32 values, then the other half's
     float mx[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) mx[t] = fmaxf(fmaxf(s[0][4 * t], s[0][4 * t + 1]), fmaxf(s[0][4 * t + 2], s[0][4 * t + 3]));
@@ -272,29 +316,14 @@ __device__ __forceinline__ void softmax_tile(f32x16 (&s)[Tile<D>::KB], bf16x8 (&
             mx[t] = fmaxf(fmaxf(mx[t], s[kb][4 * t]), fmaxf(fmaxf(s[kb][4 * t + 1], s[kb][4 * t + 2]), s[kb][4 * t + 3]));
     const float tile_max = half_swap_max(fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3])));
 
-    const float cand = tile_max * c_log2;
-    const bool grow = cand > m_run + kLazyLog2;      // false while cand is -inf
-    const float m_new = grow ? cand : m_run;
+    const float m_new = fmaxf(m_run, tile_max * c_log2);
     const float m_use = (m_new == -__builtin_inff()) ? 0.f : m_new;
-    // rescale (rare): only when some row of the wave moved its reference max
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);   // 1 where the max stayed
-        l_run *= alpha;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);   // 1 where the max stayed
+    l_run *= alpha;
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
-    }
-    m_run = m_new;
-
-    float ps[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][i], c_log2, -m_use));
-            ps[i & 3] += p;
-            pb[2 * kb + (i >> 3)][i & 7] = (__bf16)p;
-        }
-    l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
+    m_run = m_use;
+    l_run += exp_tile<D>(s, pb, m_use, c_log2);
 }
 
 // c_log2 = |scale| * log2(e) (> 0); qsign flips the sign bit of every Q
@@ -399,66 +428,78 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     f32x16 s[KB];
     bf16x8 pb[BC / 16];
 
-    // Global loads run four phases ahead of their LDS stores: load group u =
-    // (K_{u+1}, V_u) is fetched in phase 2u-2 into register set u&1 and
-    // written to LDS at the end of phase 2u+1.  Past the last tile the loads
-    // repeat the last tile (in bounds, never stored), so every step issues
-    // the same loads.
-    u32x4 kr0[T::CHUNKS_PER_THREAD], kr1[T::CHUNKS_PER_THREAD], vr0[2], vr1[2];
-    load_rows<D>(kg, 0, N, tid, kr0);
-    store_k<D>(smem + T::K0, tid, kr0);
-    load_rows<D>(kg, min(1, n_tiles - 1) * BC, N, tid, kr0);
-    load_v<D>(vg, 0, N, tid, vr0);
+    // K/V copies.  The second group copies the K tiles, the first group the
+    // V tiles, and only a group in its vector phase writes to LDS, so the
+    // matrix phases carry no copy work beyond issuing loads.  Each wave has
+    // one staging set: a group loads a tile at the start of its matrix phase
+    // and writes it to LDS at the end of its next vector phase; tile i lives
+    // in LDS buffer i&1.
+    //   K_{u+1} is loaded in phase 2u-1 and written at the end of phase 2u,
+    //   over K_{u-1}, whose last reader (second group, matrix phase u-1) ran
+    //   in phase 2u-1; it is first read in phase 2u+2.
+    //   V_u is loaded in phase 2u and written at the end of phase 2u+1, over
+    //   V_{u-2}, last read in phase 2u-1; it is first read in phase 2u+2.
+    // Past the last tile the loads repeat the last tile (in bounds, never
+    // stored), so every copy issues the same loads.
+    const int gt = idx * 64 + lane;            // thread index within the group
+    Stage<D> stg;
+    if (grp == 1) {
+        load_k<D>(kg, 0, N, gt, stg);
+        store_k<D>(smem + T::K0, gt, stg);
+        load_k<D>(kg, min(1, n_tiles - 1) * BC, N, gt, stg);
+    }
     __syncthreads();
 
     // Phases p = 0 .. 2*n_tiles+1, each closed by a workgroup barrier.  The
     // group's local phase lp = p - grp: even lp = 2t is the matrix phase t
-    // (P_{t-1} V_{t-1}, then S_t), odd lp = 2t+1 the softmax of S_t.  K_t is
-    // read in phases 2t (first group) and 2t+1 (second); V_t in 2t+2 and
-    // 2t+3.  K_{t+1} and V_t are written to LDS at the end of phase 2t+1,
-    // into the buffers of K_{t-1} and V_{t-2}, whose last readers finished in
-    // phase 2t-1.
-    auto phase = [&](int p) __attribute__((always_inline)) {
-        const int lp = p - grp;
-        if (lp < 0) return;
-        const int t = lp >> 1;
-        if ((lp & 1) == 0) {
-            const bool has_pv = t >= 1 && t - 1 < w_tiles;
-            const bool has_s = t < w_tiles;
-            const LDS char* vl = smem + ((t - 1) & 1 ? T::V1 : T::V0);
-            const LDS char* kl = smem + (t & 1 ? T::K1 : T::K0);
-            if (has_pv && has_s)
-                gemm_phase<D, true, true>(vl, kl, pb, qf, oacc, s, lane);
-            else if (has_pv)
-                gemm_phase<D, true, false>(vl, kl, pb, qf, oacc, s, lane);
-            else if (has_s)
-                gemm_phase<D, false, true>(vl, kl, pb, qf, oacc, s, lane);
-        } else if (t < w_tiles) {
+    // (P_{t-1} V_{t-1}, then S_t; K_t and V_{t-1} are read), odd lp = 2t+1
+    // the softmax of S_t.
+    auto matrix_phase = [&](int t) __attribute__((always_inline)) {
+        const bool has_pv = t >= 1 && t - 1 < w_tiles;
+        const bool has_s = t < w_tiles;
+        const LDS char* vl = smem + ((t - 1) & 1 ? T::V1 : T::V0);
+        const LDS char* kl = smem + (t & 1 ? T::K1 : T::K0);
+        // The wave on the same SIMD runs vector work meanwhile; a higher
+        // issue priority keeps the MFMAs from waiting behind it.
+        __builtin_amdgcn_s_setprio(kMatrixPrio);
+        if (has_pv && has_s)
+            gemm_phase<D, true, true>(vl, kl, pb, qf, oacc, s, lane);
+        else if (has_pv)
+            gemm_phase<D, true, false>(vl, kl, pb, qf, oacc, s, lane);
+        else if (has_s)
+            gemm_phase<D, false, true>(vl, kl, pb, qf, oacc, s, lane);
+        __builtin_amdgcn_s_setprio(0);
+    };
+    auto softmax_phase = [&](int t) __attribute__((always_inline)) {
+        if (t >= 0 && t < w_tiles) {
             const int key0 = t * BC;
             if ((key0 + BC > N) || (CAUSAL && key0 + BC - 1 > wq0))
-                softmax_tile<D, CAUSAL, true>(s, pb, oacc, m_run, l_run, key0, N, my_row, c_log2, lane);
+                softmax_tile<D, CAUSAL, true>(s, pb, oacc, m_run, l_run, key0, N, my_row, c_log2, lane, t == 0);
             else
-                softmax_tile<D, CAUSAL, false>(s, pb, oacc, m_run, l_run, key0, N, my_row, c_log2, lane);
+                softmax_tile<D, CAUSAL, false>(s, pb, oacc, m_run, l_run, key0, N, my_row, c_log2, lane, t == 0);
         }
     };
-    // one tile step: phases 2u and 2u+1, issuing group u+1 into (kn, vn) and
-    // storing group u from (kc, vc)
-    auto tile_pair = [&](int u, u32x4 (&kc)[T::CHUNKS_PER_THREAD], u32x4 (&vc)[2],
-                         u32x4 (&kn)[T::CHUNKS_PER_THREAD], u32x4 (&vn)[2]) __attribute__((always_inline)) {
-        load_rows<D>(kg, min(u + 2, n_tiles - 1) * BC, N, tid, kn);
-        load_v<D>(vg, min(u + 1, n_tiles - 1) * BC, N, tid, vn);
-        phase(2 * u);
+    // Phases 2u and 2u+1.
+    auto tile_pair = [&](int u) __attribute__((always_inline)) {
+        if (grp == 0) {
+            load_v<D>(vg, min(u, n_tiles - 1) * BC, N, gt, stg);
+            matrix_phase(u);
+        } else {            // vector phase of tile u-1 of the second group
+            softmax_phase(u - 1);
+            if (u + 1 < n_tiles) store_k<D>(smem + ((u + 1) & 1 ? T::K1 : T::K0), gt, stg);
+        }
         __syncthreads();
-        phase(2 * u + 1);
-        if (u + 1 < n_tiles) store_k<D>(smem + ((u + 1) & 1 ? T::K1 : T::K0), tid, kc);
-        if (u < n_tiles) store_vt<D>(smem + (u & 1 ? T::V1 : T::V0), tid, vc);
+        if (grp == 0) {     // vector phase of tile u of the first group
+            softmax_phase(u);
+            if (u < n_tiles) store_vt<D>(smem + (u & 1 ? T::V1 : T::V0), gt, stg);
+        } else {
+            load_k<D>(kg, min(u + 2, n_tiles - 1) * BC, N, gt, stg);
+            matrix_phase(u);
+        }
         __syncthreads();
     };
 #pragma unroll 1
-    for (int u = 0; u <= n_tiles; u += 2) {
-        tile_pair(u, kr0, vr0, kr1, vr1);
-        if (u + 1 <= n_tiles) tile_pair(u + 1, kr1, vr1, kr0, vr0);
-    }
+    for (int u = 0; u <= n_tiles; ++u) tile_pair(u);
 
     if (wq0 >= N) return;
     const float l_tot = half_swap_sum(l_run);
