@@ -47,6 +47,8 @@
 #ifndef FA_H
 #define FA_H
 
+#include <stddef.h>
+
 #include <hip/hip_runtime_api.h>
 
 #ifdef __cplusplus
@@ -59,8 +61,9 @@ enum fa_status {
     FA_ERR_SHAPE = -2,     /* B, Hq, Hkv or N <= 0, or the problem is too large to index */
     FA_ERR_HEADS = -3,     /* Hq is not a multiple of Hkv */
     FA_ERR_HEADDIM = -4,   /* d is not one of the supported head sizes (64, 128) */
-    FA_ERR_ARG = -5,       /* scale is not finite */
-    FA_ERR_HIP = -6        /* the HIP runtime rejected the launch */
+    FA_ERR_ARG = -5,       /* scale is not finite, or num_splits is out of range */
+    FA_ERR_HIP = -6,       /* the HIP runtime rejected the launch */
+    FA_ERR_WORKSPACE = -7  /* the split-KV workspace is null or too small */
 };
 
 /*
@@ -90,6 +93,45 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                int B, int Hq, int Hkv, int N, int d, int causal, float scale,
                hipStream_t stream);
+
+/*
+ * fa_fwd_splitkv_workspace_size - bytes of device workspace that
+ * fa_fwd_splitkv needs for these sizes: num_splits * B * Hq * N * (d + 1) * 4
+ * (a float32 partial output and a float32 partial logsumexp per split and
+ * query row).  Returns 0 for arguments that fa_fwd_splitkv would reject
+ * (non-positive sizes, d not in {64, 128}, num_splits outside 1..256).
+ */
+size_t fa_fwd_splitkv_workspace_size(int B, int Hq, int N, int d, int num_splits);
+
+/*
+ * fa_fwd_splitkv - the result of fa_fwd (same o and lse, up to float
+ * rounding order), computed as num_splits independent passes over disjoint
+ * ranges of the keys followed by a merge.  This is the per-block rescaling
+ * of the reading-notes page (Methods, the two rescaling equations) applied
+ * to whole key ranges: each pass produces a partial output O_s (normalised by
+ * its own row sum) and a partial logsumexp LSE_s, and the merge forms
+ * LSE = ln sum_s exp(LSE_s) and O = sum_s exp(LSE_s - LSE) O_s.  More passes
+ * give more independent workgroups, which fills the GPU when B * Hq * N is
+ * small.
+ *
+ * Arguments q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, stream: as for
+ *   fa_fwd (bf16 inputs and output, float32 lse).
+ * num_splits: 1..256.  The keys are cut into 64-key tiles and split s takes
+ *   tiles [s*T/num_splits, (s+1)*T/num_splits) of the T = ceil(N/64) tiles;
+ *   more splits than tiles leave some ranges empty, which is allowed.
+ * workspace: device memory of at least workspace_bytes bytes, owned by the
+ *   caller, 16-byte aligned; workspace_bytes must be at least
+ *   fa_fwd_splitkv_workspace_size(B, Hq, N, d, num_splits).  Its contents on
+ *   entry do not matter and are overwritten; it must not be used by another
+ *   call that runs at the same time.
+ * Both kernels are enqueued on `stream`; the library allocates nothing.
+ * Returns FA_OK or a negative fa_status (FA_ERR_ARG for num_splits,
+ * FA_ERR_WORKSPACE for a null or small workspace).
+ */
+int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                   int num_splits, void* workspace, size_t workspace_bytes,
+                   hipStream_t stream);
 
 /*
  * fa_status_string - a static, human-readable description of a status code

@@ -66,6 +66,44 @@ extern "C" int fa_fwd_f32(const float* q, const float* k, const float* v, float*
     return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+namespace {
+
+// Split count and workspace checks of the split-KV entry point (after the
+// common validation).
+int validate_split(int B, int Hq, int N, int d, int num_splits, const void* workspace,
+                   size_t workspace_bytes) {
+    if (num_splits < 1 || num_splits > fa::kMaxSplits) return FA_ERR_ARG;
+    const long long bh = (long long)B * Hq;
+    const long long qtiles = ((long long)N + fa::kBlockRowsBf16 - 1) / fa::kBlockRowsBf16;
+    if (bh * qtiles * num_splits > INT_MAX) return FA_ERR_SHAPE;
+    if (!workspace) return FA_ERR_WORKSPACE;
+    const long long need = fa::split_workspace_floats(B, Hq, N, d, num_splits) * 4;
+    if ((unsigned long long)need > (unsigned long long)workspace_bytes) return FA_ERR_WORKSPACE;
+    return FA_OK;
+}
+
+}  // namespace
+
+extern "C" size_t fa_fwd_splitkv_workspace_size(int B, int Hq, int N, int d, int num_splits) {
+    if (B <= 0 || Hq <= 0 || N <= 0 || (d != 64 && d != 128)) return 0;
+    if (num_splits < 1 || num_splits > fa::kMaxSplits) return 0;
+    if ((double)B * Hq * (double)N * 128.0 >= 1125899906842624.0) return 0;
+    return (size_t)fa::split_workspace_floats(B, Hq, N, d, num_splits) * 4;
+}
+
+extern "C" int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                              int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                              int num_splits, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream) {
+    int rc = validate(q, k, v, o, lse, B, Hq, Hkv, N, d, scale);
+    if (rc != FA_OK) return rc;
+    rc = validate_split(B, Hq, N, d, num_splits, workspace, workspace_bytes);
+    if (rc != FA_OK) return rc;
+    const hipError_t e = fa::launch_fwd_bf16_split(pack(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale),
+                                                   num_splits, (float*)workspace, stream);
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 extern "C" const char* fa_status_string(int status) {
     switch (status) {
         case FA_OK: return "ok";
@@ -73,7 +111,8 @@ extern "C" const char* fa_status_string(int status) {
         case FA_ERR_SHAPE: return "invalid shape (B, Hq, Hkv and N must be positive and the problem indexable)";
         case FA_ERR_HEADS: return "Hq must be a multiple of Hkv";
         case FA_ERR_HEADDIM: return "unsupported head size d (supported: 64, 128)";
-        case FA_ERR_ARG: return "scale must be finite";
+        case FA_ERR_ARG: return "invalid scalar argument (scale must be finite, num_splits in 1..256)";
+        case FA_ERR_WORKSPACE: return "workspace is null or smaller than fa_fwd_splitkv_workspace_size()";
         case FA_ERR_HIP: return "HIP launch failed";
         default: return "unknown status";
     }

@@ -328,11 +328,19 @@ __device__ __forceinline__ void softmax_tile(f32x16 (&s)[Tile<D>::KB], bf16x8 (&
 
 // c_log2 = |scale| * log2(e) (> 0); qsign flips the sign bit of every Q
 // element when scale < 0 (exact), so that the kernel only sees c_log2 > 0.
-template <int D, bool CAUSAL>
+//
+// SPLIT: the launch covers n_splits disjoint ranges of the n_kt key tiles
+// (split s takes tiles [s*n_kt/n_splits, (s+1)*n_kt/n_splits)), split-major
+// over the block index.  Each workgroup then writes the fp32 partial result
+// of its range instead of O and LSE: the output normalised by its own row
+// sum to OP[s][bh][row][d], and the logsumexp of its range to LP[s][bh][row]
+// (O = 0 and LSE = -inf for a row that sees no key of the range).
+template <int D, bool CAUSAL, bool SPLIT>
 __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     __bf16* __restrict__ O, float* __restrict__ LSE, int group, int N, int n_qtiles, int bh_total,
-    float c_log2, uint32_t qsign) {
+    float c_log2, uint32_t qsign, int n_splits, int n_kt, float* __restrict__ OP,
+    float* __restrict__ LP) {
     using T = Tile<D>;
     constexpr int BC = T::BC;
     constexpr int KB = T::KB;
@@ -356,8 +364,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     // latest (heaviest, when causal) tiles first, so the short tiles fill the
     // tail of the launch.
     int bh, qt;
+    const int split = SPLIT ? (int)blockIdx.x / (bh_total * n_qtiles) : 0;
     {
-        const int w = blockIdx.x;
+        const int w = SPLIT ? (int)blockIdx.x % (bh_total * n_qtiles) : (int)blockIdx.x;
         if ((bh_total & 7) == 0) {
             const int slot = w >> 3;
             bh = (w & 7) * (bh_total >> 3) + slot % (bh_total >> 3);
@@ -412,13 +421,17 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
         }
     }
 
+    // Key tiles: local tile t is global tile kt_lo + t (kt_lo = 0 unless SPLIT).
+    const int kt_lo = SPLIT ? (int)((long long)split * n_kt / n_splits) : 0;
+    const int kt_hi = SPLIT ? (int)((long long)(split + 1) * n_kt / n_splits) : n_kt;
     const int kv_end = CAUSAL ? min(N, q0 + kBr) : N;       // keys this workgroup needs
-    const int n_tiles = (kv_end + BC - 1) / BC;
+    const int n_tiles = max(0, min(kt_hi, (kv_end + BC - 1) / BC) - kt_lo);
     const int w_kv_end = CAUSAL ? min(N, wq0 + kWaveRows) : N;
-    const int w_tiles = (wq0 < N) ? (w_kv_end + BC - 1) / BC : 0;   // tiles this wave computes
+    const int w_tiles = (wq0 < N) ? max(0, min(kt_hi, (w_kv_end + BC - 1) / BC) - kt_lo) : 0;
 
-    const u32x4* kg = (const u32x4*)(K + kv_head);
-    const u32x4* vg = (const u32x4*)(V + kv_head);
+    const u32x4* kg = (const u32x4*)(K + kv_head + (size_t)kt_lo * BC * D);
+    const u32x4* vg = (const u32x4*)(V + kv_head + (size_t)kt_lo * BC * D);
+    const int Nl = N - kt_lo * BC;           // keys from the first tile of the range on
 
     f32x16 oacc[DB];
 #pragma unroll
@@ -442,11 +455,24 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     // Past the last tile the loads repeat the last tile (in bounds, never
     // stored), so every copy issues the same loads.
     const int gt = idx * 64 + lane;            // thread index within the group
+    if (SPLIT && n_tiles == 0) {               // no key of the range is visible to the tile
+        if (my_row < N && wq0 < N) {
+            const size_t prow = ((size_t)split * bh_total + bh) * N + my_row;
+            float* opp = OP + prow * D;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    *(float4*)(opp + 32 * db + 8 * g + 4 * h) = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (h == 0) LP[prow] = -__builtin_inff();
+        }
+        return;
+    }
     Stage<D> stg;
     if (grp == 1) {
-        load_k<D>(kg, 0, N, gt, stg);
+        load_k<D>(kg, 0, Nl, gt, stg);
         store_k<D>(smem + T::K0, gt, stg);
-        load_k<D>(kg, min(1, n_tiles - 1) * BC, N, gt, stg);
+        load_k<D>(kg, min(1, n_tiles - 1) * BC, Nl, gt, stg);
     }
     __syncthreads();
 
@@ -472,7 +498,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     };
     auto softmax_phase = [&](int t) __attribute__((always_inline)) {
         if (t >= 0 && t < w_tiles) {
-            const int key0 = t * BC;
+            const int key0 = (kt_lo + t) * BC;
             if ((key0 + BC > N) || (CAUSAL && key0 + BC - 1 > wq0))
                 softmax_tile<D, CAUSAL, true>(s, pb, oacc, m_run, l_run, key0, N, my_row, c_log2, lane, t == 0);
             else
@@ -482,7 +508,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     // Phases 2u and 2u+1.
     auto tile_pair = [&](int u) __attribute__((always_inline)) {
         if (grp == 0) {
-            load_v<D>(vg, min(u, n_tiles - 1) * BC, N, gt, stg);
+            load_v<D>(vg, min(u, n_tiles - 1) * BC, Nl, gt, stg);
             matrix_phase(u);
         } else {            // vector phase of tile u-1 of the second group
             softmax_phase(u - 1);
@@ -493,7 +519,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
             softmax_phase(u);
             if (u < n_tiles) store_vt<D>(smem + (u & 1 ? T::V1 : T::V0), gt, stg);
         } else {
-            load_k<D>(kg, min(u + 2, n_tiles - 1) * BC, N, gt, stg);
+            load_k<D>(kg, min(u + 2, n_tiles - 1) * BC, Nl, gt, stg);
             matrix_phase(u);
         }
         __syncthreads();
@@ -504,6 +530,22 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     if (wq0 >= N) return;
     const float l_tot = half_swap_sum(l_run);
     if (my_row >= N) return;
+    if constexpr (SPLIT) {
+        const bool seen = l_tot > 0.f;       // the row saw some key of the range
+        const float inv = seen ? 1.f / l_tot : 0.f;
+        const size_t prow = ((size_t)split * bh_total + bh) * N + my_row;
+        float* opp = OP + prow * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                *(float4*)(opp + 32 * db + 8 * g + 4 * h) =
+                    make_float4(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv,
+                                oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
+        if (h == 0)
+            LP[prow] = seen ? (m_run + __builtin_log2f(l_tot)) * 0.69314718055994531f : -__builtin_inff();
+        return;
+    }
     const float inv = 1.f / l_tot;
     __bf16* op = O + q_head + (size_t)my_row * D;
 #pragma unroll
@@ -519,9 +561,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     if (h == 0) LSE[(size_t)bh * N + my_row] = (m_run + __builtin_log2f(l_tot)) * 0.69314718055994531f;
 }
 
-template <int D, bool CAUSAL>
-hipError_t launch(const FwdArgs& a, hipStream_t stream) {
+template <int D, bool CAUSAL, bool SPLIT>
+hipError_t launch(const FwdArgs& a, int n_splits, float* op, float* lp, hipStream_t stream) {
     const int n_qtiles = (a.N + kBr - 1) / kBr;
+    int n_kt = (a.N + Tile<D>::BC - 1) / Tile<D>::BC;
     const int bh_total = a.B * a.Hq;
     float c_log2 = fabsf(a.scale) * 1.4426950408889634f;
     // A zero scale makes every weight equal; a tiny positive factor gives the
@@ -536,16 +579,86 @@ hipError_t launch(const FwdArgs& a, hipStream_t stream) {
     const __bf16* v = (const __bf16*)a.v;
     __bf16* o = (__bf16*)a.o;
     float* lse = a.lse;
-    void* args[] = {&q, &k, &v, &o, &lse, &group, &N, (void*)&n_qtiles, (void*)&bh_total, &c_log2, &qsign};
-    return hipLaunchKernel((const void*)fwd_bf16_kernel<D, CAUSAL>, dim3(bh_total * n_qtiles),
-                           dim3(kThreads), args, 0, stream);
+    void* args[] = {&q, &k, &v, &o, &lse, &group, &N, (void*)&n_qtiles, (void*)&bh_total,
+                    &c_log2, &qsign, &n_splits, &n_kt, &op, &lp};
+    return hipLaunchKernel((const void*)fwd_bf16_kernel<D, CAUSAL, SPLIT>,
+                           dim3((SPLIT ? n_splits : 1) * bh_total * n_qtiles), dim3(kThreads), args, 0,
+                           stream);
+}
+
+// Merge of the split partials: the reading-notes page's rescaling rule
+// (Methods, the two rescaling equations) applied to whole ranges.  With
+// LSE = ln sum_s exp(LSE_s), O = sum_s exp(LSE_s - LSE) O_s.  One thread per
+// (row, 4 consecutive d); kMergeRows rows per 256-thread block.
+constexpr int kMergeThreads = 256;
+
+template <int D>
+__global__ __launch_bounds__(kMergeThreads) void merge_splits_kernel(
+    const float* __restrict__ OP, const float* __restrict__ LP, __bf16* __restrict__ O,
+    float* __restrict__ LSE, int n_splits, long long rows) {
+    constexpr int TPR = D / 4;                        // threads per row
+    const long long row = (long long)blockIdx.x * (kMergeThreads / TPR) + threadIdx.x / TPR;
+    if (row >= rows) return;
+    const int c4 = threadIdx.x % TPR;
+    float mx = -__builtin_inff();
+    for (int sp = 0; sp < n_splits; ++sp) mx = fmaxf(mx, LP[sp * rows + row]);
+    float wsum = 0.f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int sp = 0; sp < n_splits; ++sp) {
+        const float l = LP[sp * rows + row];
+        const float w = l == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f((l - mx) * 1.4426950408889634f);
+        const float4 x = *(const float4*)(OP + (sp * rows + row) * D + 4 * c4);
+        wsum += w;
+        acc.x += w * x.x;
+        acc.y += w * x.y;
+        acc.z += w * x.z;
+        acc.w += w * x.w;
+    }
+    const float inv = 1.f / wsum;
+    bf16x4 out;
+    out[0] = (__bf16)(acc.x * inv);
+    out[1] = (__bf16)(acc.y * inv);
+    out[2] = (__bf16)(acc.z * inv);
+    out[3] = (__bf16)(acc.w * inv);
+    *(bf16x4*)(O + row * D + 4 * c4) = out;
+    if (c4 == 0) LSE[row] = mx + __builtin_logf(wsum);
+}
+
+template <int D>
+hipError_t launch_merge(const FwdArgs& a, int n_splits, const float* op, const float* lp,
+                        hipStream_t stream) {
+    long long rows = (long long)a.B * a.Hq * a.N;
+    const long long per_block = kMergeThreads / (D / 4);
+    __bf16* o = (__bf16*)a.o;
+    float* lse = a.lse;
+    void* args[] = {(void*)&op, (void*)&lp, &o, &lse, &n_splits, &rows};
+    return hipLaunchKernel((const void*)merge_splits_kernel<D>, dim3((unsigned)((rows + per_block - 1) / per_block)),
+                           dim3(kMergeThreads), args, 0, stream);
 }
 
 }  // namespace
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
-    if (a.d == 128) return a.causal ? launch<128, true>(a, stream) : launch<128, false>(a, stream);
-    return a.causal ? launch<64, true>(a, stream) : launch<64, false>(a, stream);
+    if (a.d == 128)
+        return a.causal ? launch<128, true, false>(a, 1, nullptr, nullptr, stream)
+                        : launch<128, false, false>(a, 1, nullptr, nullptr, stream);
+    return a.causal ? launch<64, true, false>(a, 1, nullptr, nullptr, stream)
+                    : launch<64, false, false>(a, 1, nullptr, nullptr, stream);
+}
+
+hipError_t launch_fwd_bf16_split(const FwdArgs& a, int n_splits, float* workspace, hipStream_t stream) {
+    float* op = workspace;
+    float* lp = workspace + (size_t)n_splits * a.B * a.Hq * a.N * a.d;
+    hipError_t e;
+    if (a.d == 128)
+        e = a.causal ? launch<128, true, true>(a, n_splits, op, lp, stream)
+                     : launch<128, false, true>(a, n_splits, op, lp, stream);
+    else
+        e = a.causal ? launch<64, true, true>(a, n_splits, op, lp, stream)
+                     : launch<64, false, true>(a, n_splits, op, lp, stream);
+    if (e != hipSuccess) return e;
+    return a.d == 128 ? launch_merge<128>(a, n_splits, op, lp, stream)
+                      : launch_merge<64>(a, n_splits, op, lp, stream);
 }
 
 }  // namespace fa

@@ -18,11 +18,25 @@ struct FwdArgs {
 
 // Each returns hipSuccess or the launch error.
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
+// Split-KV form of launch_fwd_bf16: partials of n_splits key ranges into
+// `workspace` (float32, split_workspace_floats(...) elements), then a merge
+// into a.o and a.lse.  Both kernels are enqueued on `stream`.
+hipError_t launch_fwd_bf16_split(const FwdArgs& a, int n_splits, float* workspace, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
 
 // Query rows per workgroup of the bf16 kernel (the grid is B*Hq*ceil(N/kBlockRowsBf16)).
 constexpr int kBlockRowsBf16 = 256;
 // Query rows per workgroup of the fp32 kernel.
 constexpr int kBlockRowsF32 = 64;
+// Keys per tile of the bf16 kernel (the granularity of split-KV ranges).
+constexpr int kKeyTileBf16 = 64;
+// Largest split count of the split-KV entry point.
+constexpr int kMaxSplits = 256;
+
+// float32 elements of the split-KV workspace: partial O then partial LSE.
+inline long long split_workspace_floats(long long B, long long Hq, long long N, long long d,
+                                        long long n_splits) {
+    return n_splits * B * Hq * N * (d + 1);
+}
 
 }  // namespace fa

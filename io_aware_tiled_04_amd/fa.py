@@ -4,10 +4,12 @@ Only argument marshalling lives here: every step of the forward pass runs in
 the HIP kernels of ``libfa.so``.  There is no fallback: if the library is
 missing or cannot be loaded, importing this module raises.
 
-``fa_fwd``, ``fa_fwd_f32`` and ``fa_status_string`` have the C names and
-arguments (integer device pointers, sizes, stream handle).  ``fwd`` is the
-torch-facing convenience: it checks the tensors, allocates O and LSE on the
-inputs' device and launches on torch's current stream.
+``fa_fwd``, ``fa_fwd_f32``, ``fa_fwd_splitkv``,
+``fa_fwd_splitkv_workspace_size`` and ``fa_status_string`` have the C names
+and arguments (integer device pointers, sizes, stream handle).  ``fwd`` and
+``fwd_splitkv`` are the torch-facing conveniences: they check the tensors,
+allocate O, LSE (and the split-KV workspace) on the inputs' device and launch
+on torch's current stream.
 """
 from __future__ import annotations
 
@@ -25,9 +27,11 @@ FA_ERR_HEADS = -3
 FA_ERR_HEADDIM = -4
 FA_ERR_ARG = -5
 FA_ERR_HIP = -6
+FA_ERR_WORKSPACE = -7
 
 # Names declared in include/fa.h, in order.
-EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_status_string")
+EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_fwd_splitkv_workspace_size", "fa_fwd_splitkv",
+           "fa_status_string")
 
 
 def _load():
@@ -41,6 +45,11 @@ def _load():
         fn = getattr(lib, name)
         fn.argtypes = fwd_args
         fn.restype = ctypes.c_int
+    lib.fa_fwd_splitkv.argtypes = fwd_args[:-1] + [ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t,
+                                                   ctypes.c_void_p]
+    lib.fa_fwd_splitkv.restype = ctypes.c_int
+    lib.fa_fwd_splitkv_workspace_size.argtypes = [ctypes.c_int] * 5
+    lib.fa_fwd_splitkv_workspace_size.restype = ctypes.c_size_t
     lib.fa_status_string.argtypes = [ctypes.c_int]
     lib.fa_status_string.restype = ctypes.c_char_p
     return lib
@@ -67,6 +76,18 @@ def fa_fwd(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, stream) -> int:
 def fa_fwd_f32(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, stream) -> int:
     """Raw call of the fp32 C entry point; pointers and stream are integers."""
     return _lib.fa_fwd_f32(q, k, v, o, lse, B, Hq, Hkv, N, d, int(causal), float(scale), stream)
+
+
+def fa_fwd_splitkv_workspace_size(B, Hq, N, d, num_splits) -> int:
+    """Bytes of workspace the split-KV entry point needs (0 for invalid sizes)."""
+    return int(_lib.fa_fwd_splitkv_workspace_size(B, Hq, N, d, num_splits))
+
+
+def fa_fwd_splitkv(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, num_splits, workspace,
+                   workspace_bytes, stream) -> int:
+    """Raw call of the split-KV C entry point; pointers and stream are integers."""
+    return _lib.fa_fwd_splitkv(q, k, v, o, lse, B, Hq, Hkv, N, d, int(causal), float(scale),
+                               int(num_splits), workspace, int(workspace_bytes), stream)
 
 
 def _check(t, name, dtype, device):
@@ -114,6 +135,43 @@ def fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse
     fn = fa_fwd if dtype == torch.bfloat16 else fa_fwd_f32
     rc = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
             B, Hq, Hkv, N, d, causal, scale, s)
+    if rc != FA_OK:
+        raise FaError(rc)
+    return o, lse
+
+
+def fwd_splitkv(q, k, v, num_splits: int, causal: bool = False, scale: float | None = None,
+                workspace=None, stream=None):
+    """Split-KV attention forward on bf16 tensors: returns (O, LSE), the same
+    result as ``fwd`` up to float rounding order.
+
+    ``workspace`` is an optional uint8 device tensor of at least
+    ``fa_fwd_splitkv_workspace_size(...)`` bytes; one is allocated when it is
+    None.  Launches on ``stream`` or torch's current stream.
+    """
+    import torch
+    dev = q.device
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, n, torch.bfloat16, dev)
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    if tuple(k.shape) != (B, Hkv, N, d) or tuple(v.shape) != (B, Hkv, N, d):
+        raise ValueError("k and v must be [B, Hkv, N, d] with q's B, N and d")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = fa_fwd_splitkv_workspace_size(B, Hq, N, d, num_splits)
+    if need == 0:
+        raise ValueError("invalid sizes or num_splits for the split-KV forward")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on q's device")
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
+    s = (stream if stream is not None else torch.cuda.current_stream(dev)).cuda_stream
+    rc = fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                        B, Hq, Hkv, N, d, causal, scale, num_splits, workspace.data_ptr(),
+                        workspace.numel() * workspace.element_size(), s)
     if rc != FA_OK:
         raise FaError(rc)
     return o, lse

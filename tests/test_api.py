@@ -20,7 +20,8 @@ def _declared():
 
 
 def test_header_declares_the_entry_points():
-    assert _declared() == ["fa_fwd", "fa_fwd_f32", "fa_status_string"]
+    assert _declared() == ["fa_fwd", "fa_fwd_f32", "fa_fwd_splitkv_workspace_size",
+                           "fa_fwd_splitkv", "fa_status_string"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -68,6 +69,48 @@ def test_invalid_arguments_are_rejected(fn, args, expect):
     from io_aware_tiled_04_amd import fa
     rc = getattr(fa, fn)(*args, 0)
     assert rc == getattr(fa, expect), (rc, fa.fa_status_string(rc))
+
+
+def test_splitkv_rejects_the_common_invalid_arguments():
+    """The split-KV entry point runs the same validation as fa_fwd first."""
+    from io_aware_tiled_04_amd import fa
+    W = 1 << 30
+    cases = [
+        ((0, P, P, P, P, 1, 1, 1, 128, 64, 0, 0.125), "FA_ERR_NULL"),
+        ((P, P, P, P, 0, 1, 1, 1, 128, 64, 0, 0.125), "FA_ERR_NULL"),
+        ((P, P, P, P, P, 1, 1, 1, 0, 64, 0, 0.125), "FA_ERR_SHAPE"),
+        ((P, P, P, P, P, 1, 6, 4, 128, 64, 1, 0.125), "FA_ERR_HEADS"),
+        ((P, P, P, P, P, 1, 1, 1, 128, 80, 1, 0.125), "FA_ERR_HEADDIM"),
+        ((P, P, P, P, P, 1, 1, 1, 128, 64, 1, math.nan), "FA_ERR_ARG"),
+    ]
+    for args, expect in cases:
+        rc = fa.fa_fwd_splitkv(*args, 2, P, W, 0)
+        assert rc == getattr(fa, expect), (args, rc)
+
+
+@pytest.mark.parametrize("splits,ws,wbytes,expect", [
+    (0, P, 1 << 30, "FA_ERR_ARG"),
+    (-3, P, 1 << 30, "FA_ERR_ARG"),
+    (257, P, 1 << 30, "FA_ERR_ARG"),
+    (2, 0, 1 << 30, "FA_ERR_WORKSPACE"),
+    (2, P, 0, "FA_ERR_WORKSPACE"),
+    # 2 splits of [1, 4, 300, 64]: 2 * 4 * 300 * 65 * 4 bytes, one byte short
+    (2, P, 2 * 4 * 300 * 65 * 4 - 1, "FA_ERR_WORKSPACE"),
+])
+def test_splitkv_checks_splits_and_workspace(splits, ws, wbytes, expect):
+    from io_aware_tiled_04_amd import fa
+    rc = fa.fa_fwd_splitkv(P, P, P, P, P, 1, 4, 2, 300, 64, 1, 0.125, splits, ws, wbytes, 0)
+    assert rc == getattr(fa, expect), (rc, fa.fa_status_string(rc))
+
+
+def test_splitkv_workspace_size():
+    from io_aware_tiled_04_amd import fa
+    assert fa.fa_fwd_splitkv_workspace_size(1, 4, 300, 64, 2) == 2 * 4 * 300 * 65 * 4
+    assert fa.fa_fwd_splitkv_workspace_size(2, 32, 4096, 128, 3) == 3 * 64 * 4096 * 129 * 4
+    assert fa.fa_fwd_splitkv_workspace_size(1, 1, 1, 128, 1) == 129 * 4
+    for bad in [(0, 4, 300, 64, 2), (1, 0, 300, 64, 2), (1, 4, 0, 64, 2), (1, 4, 300, 96, 2),
+                (1, 4, 300, 64, 0), (1, 4, 300, 64, 257)]:
+        assert fa.fa_fwd_splitkv_workspace_size(*bad) == 0, bad
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
