@@ -5,6 +5,7 @@ inputs of the headline workload: causal bf16 attention, B=2, H=32, N=4096,
 d=128 (seeded synthetic data).  Prints one JSON line.
 
   python bench.py [--steps K] [--warmup W] [--config c3] [--no-cpu-baseline]
+  python bench.py --splitkv S [--config s1]   (split-KV path against the direct one)
 
 FLOPs per launch are the nominal 4*B*H*N^2*d, halved for causal.  The roofline
 entry compares the average launch duration (HIP events around every launch on
@@ -133,11 +134,14 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="c3")
+    ap.add_argument("--config", default=None,
+                    help="workload (default c3; s1 with --splitkv)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--summarize", default=None)
+    ap.add_argument("--splitkv", type=int, default=0,
+                    help="time fa_fwd_splitkv with this many splits (and fa_fwd beside it)")
     args = ap.parse_args()
 
     if args.summarize:
@@ -154,9 +158,11 @@ def main() -> int:
 
     import oracle
     from io_aware_tiled_04_amd import fa
-    from io_aware_tiled_04_amd.workloads import CONFIGS, as_f64_numpy, make_inputs
+    from io_aware_tiled_04_amd.workloads import CONFIGS, EXTRA, as_f64_numpy, make_inputs
 
-    w = CONFIGS[args.config]
+    if args.splitkv:
+        return bench_splitkv(args)
+    w = CONFIGS[args.config or "c3"]
     if w.dtype != "bf16":
         print("the bench times the bf16 entry point; pick a bf16 configuration", file=sys.stderr)
         return 2
@@ -254,6 +260,102 @@ def main() -> int:
         out["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_seconds)
     print(json.dumps(out), flush=True)
     return 0 if parity_ok else 1
+
+
+def _time_launches(launch, stream, steps, warmup):
+    """Average per-launch milliseconds (HIP events on the launch stream) and
+    the timed region's total milliseconds."""
+    import torch
+    for _ in range(warmup):
+        launch()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    r0 = torch.cuda.Event(enable_timing=True)
+    r1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    r0.record(stream)
+    for i in range(steps):
+        starts[i].record(stream)
+        launch()
+        ends[i].record(stream)
+    r1.record(stream)
+    torch.cuda.synchronize()
+    per = [a.elapsed_time(b) for a, b in zip(starts, ends)]
+    return sum(per) / len(per), r0.elapsed_time(r1)
+
+
+def bench_splitkv(args) -> int:
+    """fa_fwd_splitkv against fa_fwd on the same resident inputs; one JSON line.
+    The merge kernel is HBM-bound: its algorithmic bytes are the partials read
+    once (S * rows * (d + 1) * 4) plus O and LSE written once."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from io_aware_tiled_04_amd import fa
+    from io_aware_tiled_04_amd.workloads import CONFIGS, EXTRA, as_f64_numpy, make_inputs
+
+    name = args.config or "s1"
+    w = EXTRA.get(name) or CONFIGS[name]
+    S = args.splitkv
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q, k, v = make_inputs(w)
+    qd, kd, vd = (t.to(dev) for t in (q, k, v))
+    o = torch.empty_like(qd)
+    lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device=dev)
+    need = fa.fa_fwd_splitkv_workspace_size(w.B, w.Hq, w.N, w.d, S)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    ptrs = (qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(), lse.data_ptr())
+
+    def launch_split():
+        rc = fa.fa_fwd_splitkv(*ptrs, w.B, w.Hq, w.Hkv, w.N, w.d, int(w.causal), w.scale, S,
+                               ws.data_ptr(), need, stream.cuda_stream)
+        if rc != fa.FA_OK:
+            raise fa.FaError(rc)
+
+    def launch_direct():
+        rc = fa.fa_fwd(*ptrs, w.B, w.Hq, w.Hkv, w.N, w.d, int(w.causal), w.scale,
+                       stream.cuda_stream)
+        if rc != fa.FA_OK:
+            raise fa.FaError(rc)
+
+    direct_ms, _ = _time_launches(launch_direct, stream, args.steps, args.warmup)
+    split_ms, split_total = _time_launches(launch_split, stream, args.steps, args.warmup)
+
+    rng = np.random.default_rng(0)
+    rows = [(b, h, int(i)) for b in range(w.B) for h in range(w.Hq)
+            for i in [0, w.N - 1] + list(rng.integers(0, w.N, 6))]
+    o_ref, lse_ref = oracle.attention_rows(as_f64_numpy(q), as_f64_numpy(k), as_f64_numpy(v),
+                                           w.causal, w.scale, rows)
+    idx = tuple(np.array(rows).T)
+    err = np.abs(as_f64_numpy(o)[idx] - o_ref)
+    lerr = np.abs(as_f64_numpy(lse)[idx] - lse_ref)
+    ok = bool(err.max() <= 2e-2 and err.mean() <= 2e-3 and lerr.max() <= 1e-3)
+    flops = w.nominal_flops()
+    rows_total = w.B * w.Hq * w.N
+    merge_bytes = S * rows_total * (w.d + 1) * 4 + rows_total * (2 * w.d + 4)
+    out = {
+        "metric": "attention fwd TFLOP/s, split-KV path (bf16)",
+        "value": round(flops * args.steps / (split_total * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(split_total / args.steps, 5), "higher_is_better": True,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{w.name}: {w.note}", "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv,
+                   "N": w.N, "d": w.d, "causal": w.causal, "seed": w.seed, "splits": S,
+                   "flops_per_step": flops},
+        "split_avg_launch_us": round(split_ms * 1e3, 2),
+        "direct_avg_launch_us": round(direct_ms * 1e3, 2),
+        "direct_tflops": round(flops / (direct_ms * 1e-3) / 1e12, 2),
+        "speedup_vs_direct": round(direct_ms / split_ms, 3),
+        "merge_algorithmic_bytes": merge_bytes,
+        "parity": {"rows": len(rows), "max_abs_o": float(err.max()),
+                   "mean_abs_o": float(err.mean()), "max_abs_lse": float(lerr.max()), "ok": ok},
+    }
+    print(json.dumps(out), flush=True)
+    return 0 if ok else 1
 
 
 if __name__ == "__main__":

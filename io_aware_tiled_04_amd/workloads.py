@@ -72,6 +72,16 @@ CONFIGS = {
 }
 
 
+# Workloads beyond the five configurations, for the split-KV path: shapes
+# whose direct grid leaves the GPU under-filled or unbalanced.
+EXTRA = {
+    "s1": Workload("s1", 1, 4, 4, 16384, 128, True, "bf16", 6,
+                   note="few heads, long causal: 256 workgroups whose work ranges 1:64"),
+    "s2": Workload("s2", 1, 2, 2, 8192, 128, False, "bf16", 7,
+                   note="two heads, non-causal: 64 workgroups on 256 CUs"),
+}
+
+
 def make_inputs(w: Workload, device: str = "cpu"):
     """Return (q, k, v) for workload ``w``: q [B,Hq,N,d], k/v [B,Hkv,N,d],
     contiguous, in ``w``'s storage type, drawn on the CPU then moved."""
