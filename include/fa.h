@@ -63,7 +63,7 @@ enum fa_status {
     FA_ERR_HEADDIM = -4,   /* d is not one of the supported head sizes (64, 128) */
     FA_ERR_ARG = -5,       /* scale is not finite, or num_splits is out of range */
     FA_ERR_HIP = -6,       /* the HIP runtime rejected the launch */
-    FA_ERR_WORKSPACE = -7  /* the split-KV workspace is null or too small */
+    FA_ERR_WORKSPACE = -7  /* a workspace argument is null or too small */
 };
 
 /*
@@ -132,6 +132,48 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
                    int B, int Hq, int Hkv, int N, int d, int causal, float scale,
                    int num_splits, void* workspace, size_t workspace_bytes,
                    hipStream_t stream);
+
+/*
+ * fa_bwd_workspace_size - bytes of device workspace that fa_bwd needs:
+ * B * Hq * N * 4 (one float32 per query row).  Returns 0 for non-positive
+ * sizes.
+ */
+size_t fa_bwd_workspace_size(int B, int Hq, int N);
+
+/*
+ * fa_bwd - gradients of the attention forward pass (bfloat16), from its
+ * saved output and logsumexp.
+ *
+ * The derivation blog's backward sections define the operation: the
+ * standard attention backward (section 反向传播) gives
+ *   dV = P^T dO,  dS = P (.) (dO V^T - D 1^T) with D_i = sum_d dO_id O_id,
+ *   dQ = scale * dS K,  dK = scale * dS^T Q,
+ * and its FlashAttention backward (section Flash Attention 反向传播, 梯度推导)
+ * computes them without storing P: only the row statistics of the forward
+ * are kept, here the logsumexp, and P = exp(scale * q_i . k_j - LSE_i) is
+ * recomputed block by block.
+ *
+ * q, k, v, o, lse: exactly the inputs and outputs of a previous fa_fwd call
+ *   with the same B, Hq, Hkv, N, d, causal and scale (o bf16 [B,Hq,N,d],
+ *   lse float32 [B,Hq,N]).
+ * dout [B,Hq,N,d]: bfloat16 upstream gradient dL/dO.
+ * dq [B,Hq,N,d], dk [B,Hkv,N,d], dv [B,Hkv,N,d]: bfloat16 outputs, written
+ *   (not accumulated into) with the gradients rounded to nearest even from
+ *   fp32.  With GQA, dk and dv of a K/V head are the sums over the query
+ *   heads of its group.
+ * workspace: device memory of at least fa_bwd_workspace_size(B, Hq, N)
+ *   bytes, owned by the caller, 4-byte aligned; its contents on entry do not
+ *   matter; it must not be shared with a call that runs at the same time.
+ * d in {64, 128}.  Products run on bf16 matrix cores with fp32 accumulation;
+ * P and dS are rounded to bf16 for their products.
+ * All work is enqueued on `stream`.  Returns FA_OK or a negative fa_status
+ * (FA_ERR_NULL for any null pointer, FA_ERR_WORKSPACE for a null or small
+ * workspace, otherwise as fa_fwd).
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+           const void* dout, void* dq, void* dk, void* dv,
+           int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+           void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * fa_status_string - a static, human-readable description of a status code

@@ -104,6 +104,45 @@ extern "C" int fa_fwd_splitkv(const void* q, const void* k, const void* v, void*
     return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+extern "C" size_t fa_bwd_workspace_size(int B, int Hq, int N) {
+    if (B <= 0 || Hq <= 0 || N <= 0) return 0;
+    if ((double)B * Hq * (double)N * 128.0 >= 1125899906842624.0) return 0;
+    return (size_t)B * Hq * N * 4;
+}
+
+extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                      const void* dout, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int N,
+                      int d, int causal, float scale, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
+    if (!dout || !dq || !dk || !dv) return FA_ERR_NULL;
+    int rc = validate(q, k, v, o, lse, B, Hq, Hkv, N, d, scale);
+    if (rc != FA_OK) return rc;
+    const long long bh = (long long)B * Hq;
+    const long long rtiles = ((long long)N + fa::kBwdBlockRows - 1) / fa::kBwdBlockRows;
+    if (bh * rtiles > INT_MAX) return FA_ERR_SHAPE;
+    if (!workspace) return FA_ERR_WORKSPACE;
+    if ((unsigned long long)B * Hq * N * 4 > (unsigned long long)workspace_bytes) return FA_ERR_WORKSPACE;
+    fa::BwdArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.dO = dout;
+    a.lse = lse;
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.N = N;
+    a.d = d;
+    a.causal = causal != 0;
+    a.scale = scale;
+    const hipError_t e = fa::launch_bwd_bf16(a, (float*)workspace, stream);
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 extern "C" const char* fa_status_string(int status) {
     switch (status) {
         case FA_OK: return "ok";
@@ -112,7 +151,7 @@ extern "C" const char* fa_status_string(int status) {
         case FA_ERR_HEADS: return "Hq must be a multiple of Hkv";
         case FA_ERR_HEADDIM: return "unsupported head size d (supported: 64, 128)";
         case FA_ERR_ARG: return "invalid scalar argument (scale must be finite, num_splits in 1..256)";
-        case FA_ERR_WORKSPACE: return "workspace is null or smaller than fa_fwd_splitkv_workspace_size()";
+        case FA_ERR_WORKSPACE: return "workspace is null or smaller than the size the entry point needs";
         case FA_ERR_HIP: return "HIP launch failed";
         default: return "unknown status";
     }

@@ -16,6 +16,22 @@ struct FwdArgs {
     float scale;
 };
 
+// Arguments of the backward pass (validated by fa_api.cpp).
+struct BwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* o;
+    const void* dO;
+    const float* lse;
+    void* dq;
+    void* dk;
+    void* dv;
+    int B, Hq, Hkv, N, d;
+    int causal;
+    float scale;
+};
+
 // Each returns hipSuccess or the launch error.
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
 // Split-KV form of launch_fwd_bf16: partials of n_splits key ranges into
@@ -23,11 +39,16 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
 // into a.o and a.lse.  Both kernels are enqueued on `stream`.
 hipError_t launch_fwd_bf16_split(const FwdArgs& a, int n_splits, float* workspace, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
+// Backward pass: D = rowsum(dO * O) into `workspace` (B*Hq*N floats), then
+// the dQ, dK and dV kernels, all enqueued on `stream`.
+hipError_t launch_bwd_bf16(const BwdArgs& a, float* workspace, hipStream_t stream);
 
 // Query rows per workgroup of the bf16 kernel (the grid is B*Hq*ceil(N/kBlockRowsBf16)).
 constexpr int kBlockRowsBf16 = 256;
 // Query rows per workgroup of the fp32 kernel.
 constexpr int kBlockRowsF32 = 64;
+// Resident rows per workgroup of the backward kernels.
+constexpr int kBwdBlockRows = 128;
 // Keys per tile of the bf16 kernel (the granularity of split-KV ranges).
 constexpr int kKeyTileBf16 = 64;
 // Largest split count of the split-KV entry point.

@@ -31,7 +31,7 @@ FA_ERR_WORKSPACE = -7
 
 # Names declared in include/fa.h, in order.
 EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_fwd_splitkv_workspace_size", "fa_fwd_splitkv",
-           "fa_status_string")
+           "fa_bwd_workspace_size", "fa_bwd", "fa_status_string")
 
 
 def _load():
@@ -50,6 +50,11 @@ def _load():
     lib.fa_fwd_splitkv.restype = ctypes.c_int
     lib.fa_fwd_splitkv_workspace_size.argtypes = [ctypes.c_int] * 5
     lib.fa_fwd_splitkv_workspace_size.restype = ctypes.c_size_t
+    lib.fa_bwd.argtypes = [ctypes.c_void_p] * 9 + [ctypes.c_int] * 6 + \
+        [ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.fa_bwd.restype = ctypes.c_int
+    lib.fa_bwd_workspace_size.argtypes = [ctypes.c_int] * 3
+    lib.fa_bwd_workspace_size.restype = ctypes.c_size_t
     lib.fa_status_string.argtypes = [ctypes.c_int]
     lib.fa_status_string.restype = ctypes.c_char_p
     return lib
@@ -88,6 +93,18 @@ def fa_fwd_splitkv(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, num_splits,
     """Raw call of the split-KV C entry point; pointers and stream are integers."""
     return _lib.fa_fwd_splitkv(q, k, v, o, lse, B, Hq, Hkv, N, d, int(causal), float(scale),
                                int(num_splits), workspace, int(workspace_bytes), stream)
+
+
+def fa_bwd_workspace_size(B, Hq, N) -> int:
+    """Bytes of workspace the backward entry point needs (0 for invalid sizes)."""
+    return int(_lib.fa_bwd_workspace_size(B, Hq, N))
+
+
+def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, N, d, causal, scale, workspace,
+           workspace_bytes, stream) -> int:
+    """Raw call of the backward C entry point; pointers and stream are integers."""
+    return _lib.fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, N, d, int(causal),
+                       float(scale), workspace, int(workspace_bytes), stream)
 
 
 def _check(t, name, dtype, device):
@@ -175,3 +192,38 @@ def fwd_splitkv(q, k, v, num_splits: int, causal: bool = False, scale: float | N
     if rc != FA_OK:
         raise FaError(rc)
     return o, lse
+
+
+def bwd(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None, workspace=None,
+        stream=None):
+    """Gradients (dQ, dK, dV) of a bf16 forward pass from its saved o and lse
+    and the upstream gradient ``dout``; allocates the outputs (and the
+    workspace when it is None) on q's device and launches on ``stream`` or
+    torch's current stream."""
+    import torch
+    dev = q.device
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
+        _check(t, n, torch.bfloat16, dev)
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    if tuple(k.shape) != (B, Hkv, N, d) or tuple(v.shape) != (B, Hkv, N, d):
+        raise ValueError("k and v must be [B, Hkv, N, d] with q's B, N and d")
+    if tuple(o.shape) != tuple(q.shape) or tuple(dout.shape) != tuple(q.shape):
+        raise ValueError("o and dout must have q's shape")
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != (B, Hq, N):
+        raise ValueError("lse must be a contiguous fp32 [B, Hq, N] tensor")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = fa_bwd_workspace_size(B, Hq, N)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    s = (stream if stream is not None else torch.cuda.current_stream(dev)).cuda_stream
+    rc = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Hq, Hkv, N, d,
+                causal, scale, workspace.data_ptr(), workspace.numel() * workspace.element_size(), s)
+    if rc != FA_OK:
+        raise FaError(rc)
+    return dq, dk, dv

@@ -96,6 +96,16 @@ def make_inputs(w: Workload, device: str = "cpu"):
     return q, k, v
 
 
+def make_grad(w: Workload, device: str = "cpu"):
+    """Return an upstream gradient dO [B,Hq,N,d] for workload ``w``: standard
+    normal values from a generator seeded with seed + 1000 (independent of
+    the inputs), in ``w``'s storage type."""
+    g = torch.Generator("cpu").manual_seed(w.seed + 1000)
+    do = torch.randn((w.B, w.Hq, w.N, w.d), dtype=torch.float32, generator=g)
+    do = do.to(w.torch_dtype).contiguous()
+    return do.to(device) if device != "cpu" else do
+
+
 def as_f64_numpy(t):
     """Exact upcast of a (CPU or device) tensor to a float64 numpy array."""
     return t.detach().to("cpu").to(torch.float64).numpy()

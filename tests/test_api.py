@@ -21,7 +21,8 @@ def _declared():
 
 def test_header_declares_the_entry_points():
     assert _declared() == ["fa_fwd", "fa_fwd_f32", "fa_fwd_splitkv_workspace_size",
-                           "fa_fwd_splitkv", "fa_status_string"]
+                           "fa_fwd_splitkv", "fa_bwd_workspace_size", "fa_bwd",
+                           "fa_status_string"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -111,6 +112,31 @@ def test_splitkv_workspace_size():
     for bad in [(0, 4, 300, 64, 2), (1, 0, 300, 64, 2), (1, 4, 0, 64, 2), (1, 4, 300, 96, 2),
                 (1, 4, 300, 64, 0), (1, 4, 300, 64, 257)]:
         assert fa.fa_fwd_splitkv_workspace_size(*bad) == 0, bad
+
+
+@pytest.mark.parametrize("ptrs,sizes,ws,expect", [
+    ((0, P, P, P, P, P, P, P, P), (1, 2, 1, 128, 64, 1, 0.125), (P, 1 << 20), "FA_ERR_NULL"),
+    ((P, P, P, P, P, 0, P, P, P), (1, 2, 1, 128, 64, 1, 0.125), (P, 1 << 20), "FA_ERR_NULL"),
+    ((P, P, P, P, P, P, 0, P, P), (1, 2, 1, 128, 64, 1, 0.125), (P, 1 << 20), "FA_ERR_NULL"),
+    ((P, P, P, P, P, P, P, P, 0), (1, 2, 1, 128, 64, 1, 0.125), (P, 1 << 20), "FA_ERR_NULL"),
+    ((P, P, P, 0, P, P, P, P, P), (1, 2, 1, 128, 64, 1, 0.125), (P, 1 << 20), "FA_ERR_NULL"),
+    ((P,) * 9, (1, 2, 1, 0, 64, 1, 0.125), (P, 1 << 20), "FA_ERR_SHAPE"),
+    ((P,) * 9, (1, 3, 2, 128, 64, 1, 0.125), (P, 1 << 20), "FA_ERR_HEADS"),
+    ((P,) * 9, (1, 2, 1, 128, 32, 1, 0.125), (P, 1 << 20), "FA_ERR_HEADDIM"),
+    ((P,) * 9, (1, 2, 1, 128, 64, 1, math.inf), (P, 1 << 20), "FA_ERR_ARG"),
+    ((P,) * 9, (1, 2, 1, 128, 64, 1, 0.125), (0, 1 << 20), "FA_ERR_WORKSPACE"),
+    ((P,) * 9, (1, 2, 1, 128, 64, 1, 0.125), (P, 2 * 128 * 4 - 1), "FA_ERR_WORKSPACE"),
+])
+def test_backward_rejects_invalid_arguments(ptrs, sizes, ws, expect):
+    from io_aware_tiled_04_amd import fa
+    rc = fa.fa_bwd(*ptrs, *sizes, *ws, 0)
+    assert rc == getattr(fa, expect), (rc, fa.fa_status_string(rc))
+
+
+def test_backward_workspace_size():
+    from io_aware_tiled_04_amd import fa
+    assert fa.fa_bwd_workspace_size(2, 32, 4096) == 2 * 32 * 4096 * 4
+    assert fa.fa_bwd_workspace_size(0, 1, 1) == 0 and fa.fa_bwd_workspace_size(1, 1, -1) == 0
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
