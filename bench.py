@@ -6,6 +6,7 @@ d=128 (seeded synthetic data).  Prints one JSON line.
 
   python bench.py [--steps K] [--warmup W] [--config c3] [--no-cpu-baseline]
   python bench.py --splitkv S [--config s1]   (split-KV path against the direct one)
+  python bench.py --backward [--config c3]     (backward pass, fa_bwd)
 
 FLOPs per launch are the nominal 4*B*H*N^2*d, halved for causal.  The roofline
 entry compares the average launch duration (HIP events around every launch on
@@ -142,6 +143,7 @@ def main() -> int:
     ap.add_argument("--summarize", default=None)
     ap.add_argument("--splitkv", type=int, default=0,
                     help="time fa_fwd_splitkv with this many splits (and fa_fwd beside it)")
+    ap.add_argument("--backward", action="store_true", help="time the backward pass (fa_bwd)")
     args = ap.parse_args()
 
     if args.summarize:
@@ -162,6 +164,8 @@ def main() -> int:
 
     if args.splitkv:
         return bench_splitkv(args)
+    if args.backward:
+        return bench_backward(args)
     w = CONFIGS[args.config or "c3"]
     if w.dtype != "bf16":
         print("the bench times the bf16 entry point; pick a bf16 configuration", file=sys.stderr)
@@ -353,6 +357,75 @@ def bench_splitkv(args) -> int:
         "merge_algorithmic_bytes": merge_bytes,
         "parity": {"rows": len(rows), "max_abs_o": float(err.max()),
                    "mean_abs_o": float(err.mean()), "max_abs_lse": float(lerr.max()), "ok": ok},
+    }
+    print(json.dumps(out), flush=True)
+    return 0 if ok else 1
+
+
+def bench_backward(args) -> int:
+    """fa_bwd on resident inputs (the forward's O and LSE computed once
+    beforehand); one JSON line.  Nominal FLOPs: five N^2 d products per head
+    (S, dP, dV, dQ, dK), i.e. 2.5 times the forward's, halved for causal; the
+    kernels recompute S and dP (8 products), which is not credited."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from io_aware_tiled_04_amd import fa
+    from io_aware_tiled_04_amd.workloads import CONFIGS, EXTRA, as_f64_numpy, make_grad, make_inputs
+
+    name = args.config or "c3"
+    w = EXTRA.get(name) or CONFIGS[name]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q, k, v = make_inputs(w)
+    do = make_grad(w)
+    qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, do))
+    o, lse = fa.fwd(qd, kd, vd, causal=w.causal, scale=w.scale)
+    dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
+    need = fa.fa_bwd_workspace_size(w.B, w.Hq, w.N)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    ptrs = tuple(t.data_ptr() for t in (qd, kd, vd, o, lse, dod, dq, dk, dv))
+
+    def launch():
+        rc = fa.fa_bwd(*ptrs, w.B, w.Hq, w.Hkv, w.N, w.d, int(w.causal), w.scale, ws.data_ptr(),
+                       need, stream.cuda_stream)
+        if rc != fa.FA_OK:
+            raise fa.FaError(rc)
+
+    avg_ms, total_ms = _time_launches(launch, stream, args.steps, args.warmup)
+    # parity on sampled query rows of dQ (each row of dQ needs only its own row of P)
+    rng = np.random.default_rng(0)
+    q64, k64, v64, do64 = (as_f64_numpy(t) for t in (q, k, v, do))
+    b, h = 0, 0
+    hk = h // (w.Hq // w.Hkv)
+    rows = np.unique(np.concatenate([[0, w.N - 1], rng.integers(0, w.N, 14)]))
+    s = w.scale * (q64[b, h, rows] @ k64[b, hk].T)
+    if w.causal:
+        s = np.where(np.arange(w.N)[None, :] > rows[:, None], -np.inf, s)
+    p = np.exp(s - s.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    o_rows = p @ v64[b, hk]
+    dp = do64[b, h, rows] @ v64[b, hk].T
+    ds = p * (dp - np.sum(do64[b, h, rows] * o_rows, axis=1)[:, None])
+    dq_ref = w.scale * (ds @ k64[b, hk])
+    err = np.abs(as_f64_numpy(dq)[b, h, rows] - dq_ref)
+    mag = max(float(np.abs(dq_ref).max()), 1e-4)
+    ok = bool(err.max() <= 2e-2 * mag)
+    flops = 2.5 * w.nominal_flops()
+    out = {
+        "metric": "attention bwd TFLOP/s (bf16, nominal 2.5x forward FLOPs)",
+        "value": round(flops * args.steps / (total_ms * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(total_ms / args.steps, 5), "higher_is_better": True,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{w.name}: {w.note}", "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv,
+                   "N": w.N, "d": w.d, "causal": w.causal, "seed": w.seed,
+                   "flops_per_step": flops},
+        "avg_launch_us": round(avg_ms * 1e3, 2),
+        "pct_of_peak": round(100 * flops / (avg_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+        "parity": {"rows": int(len(rows)), "max_abs_dq_rel": float(err.max() / mag), "ok": ok},
     }
     print(json.dumps(out), flush=True)
     return 0 if ok else 1

@@ -338,8 +338,17 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kernel(
                 for (int ks = 0; ks < KS; ++ks)
                     y = mfma32(*(const LDS bf16x8*)(brow + 32 * ks), rf2[ks], y);
             }
-            // register i holds streamed row sr(i) = (i/4)*8 + 4*h + i%4 of the tile
+            // register i holds streamed row sr(i) = (i/4)*8 + 4*h + i%4 of the tile;
+            // the statistics of rows 8g + 4h .. +3 are one 16-byte LDS read
             const LDS float* st = (const LDS float*)(base + L::S);
+            f32x4 lse4[4], d4[4];
+            if constexpr (!RES_Q) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    lse4[g] = *(const LDS f32x4*)(st + 8 * g + 4 * h);
+                    if constexpr (MODE == kDK) d4[g] = *(const LDS f32x4*)(st + kTile + 8 * g + 4 * h);
+                }
+            }
             bf16x8 w[2];
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
@@ -353,8 +362,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kernel(
                     key = srow;
                     qry = my_row;
                 } else {
-                    lse2 = st[sr];
-                    dv = st[kTile + sr];
+                    lse2 = lse4[i >> 2][i & 3];
+                    dv = MODE == kDK ? d4[i >> 2][i & 3] : 0.f;
                     key = my_row;
                     qry = srow;
                 }
