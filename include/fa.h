@@ -116,9 +116,11 @@ size_t fa_fwd_splitkv_workspace_size(int B, int Hq, int N, int d, int num_splits
  *
  * Arguments q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, stream: as for
  *   fa_fwd (bf16 inputs and output, float32 lse).
- * num_splits: 1..256.  The keys are cut into 64-key tiles and split s takes
- *   tiles [s*T/num_splits, (s+1)*T/num_splits) of the T = ceil(N/64) tiles;
- *   more splits than tiles leave some ranges empty, which is allowed.
+ * num_splits: 1..256.  The keys are cut into T = ceil(N/64) tiles of 64
+ *   keys, and the splits take consecutive ranges of them: with q = T /
+ *   num_splits and r = T % num_splits, the first r splits take q + 1 tiles
+ *   and the others q.  More splits than tiles leave some ranges empty, which
+ *   is allowed.
  * workspace: device memory of at least workspace_bytes bytes, owned by the
  *   caller, 16-byte aligned; workspace_bytes must be at least
  *   fa_fwd_splitkv_workspace_size(B, Hq, N, d, num_splits).  Its contents on

@@ -329,9 +329,10 @@ __device__ __forceinline__ void softmax_tile(f32x16 (&s)[Tile<D>::KB], bf16x8 (&
 // c_log2 = |scale| * log2(e) (> 0); qsign flips the sign bit of every Q
 // element when scale < 0 (exact), so that the kernel only sees c_log2 > 0.
 //
-// SPLIT: the launch covers n_splits disjoint ranges of the n_kt key tiles
-// (split s takes tiles [s*n_kt/n_splits, (s+1)*n_kt/n_splits)), split-major
-// over the block index.  Each workgroup then writes the fp32 partial result
+// SPLIT: the launch covers n_splits disjoint ranges of the T key tiles:
+// with kq = T / n_splits and kr = T % n_splits, split s = blockIdx.y takes
+// the tiles [s*kq + min(s, kr), (s+1)*kq + min(s+1, kr)) (kr ranges of kq+1
+// tiles, then ranges of kq).  Without SPLIT, kq = T and kr = 0.  Each workgroup then writes the fp32 partial result
 // of its range instead of O and LSE: the output normalised by its own row
 // sum to OP[s][bh][row][d], and the logsumexp of its range to LP[s][bh][row]
 // (O = 0 and LSE = -inf for a row that sees no key of the range).
@@ -339,8 +340,7 @@ template <int D, bool CAUSAL, bool SPLIT>
 __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     __bf16* __restrict__ O, float* __restrict__ LSE, int group, int N, int n_qtiles, int bh_total,
-    float c_log2, uint32_t qsign, int n_splits, int n_kt, float* __restrict__ OP,
-    float* __restrict__ LP) {
+    float c_log2, uint32_t qsign, int kq, int kr, float* __restrict__ OP, float* __restrict__ LP) {
     using T = Tile<D>;
     constexpr int BC = T::BC;
     constexpr int KB = T::KB;
@@ -364,9 +364,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     // latest (heaviest, when causal) tiles first, so the short tiles fill the
     // tail of the launch.
     int bh, qt;
-    const int split = SPLIT ? (int)blockIdx.x / (bh_total * n_qtiles) : 0;
+    const int split = SPLIT ? (int)blockIdx.y : 0;
     {
-        const int w = SPLIT ? (int)blockIdx.x % (bh_total * n_qtiles) : (int)blockIdx.x;
+        const int w = blockIdx.x;
         if ((bh_total & 7) == 0) {
             const int slot = w >> 3;
             bh = (w & 7) * (bh_total >> 3) + slot % (bh_total >> 3);
@@ -422,8 +422,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     }
 
     // Key tiles: local tile t is global tile kt_lo + t (kt_lo = 0 unless SPLIT).
-    const int kt_lo = SPLIT ? (int)((long long)split * n_kt / n_splits) : 0;
-    const int kt_hi = SPLIT ? (int)((long long)(split + 1) * n_kt / n_splits) : n_kt;
+    const int kt_lo = split * kq + min(split, kr);
+    const int kt_hi = kt_lo + kq + (split < kr ? 1 : 0);
     const int kv_end = CAUSAL ? min(N, q0 + kBr) : N;       // keys this workgroup needs
     const int n_tiles = max(0, min(kt_hi, (kv_end + BC - 1) / BC) - kt_lo);
     const int w_kv_end = CAUSAL ? min(N, wq0 + kWaveRows) : N;
@@ -564,7 +564,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
 template <int D, bool CAUSAL, bool SPLIT>
 hipError_t launch(const FwdArgs& a, int n_splits, float* op, float* lp, hipStream_t stream) {
     const int n_qtiles = (a.N + kBr - 1) / kBr;
-    int n_kt = (a.N + Tile<D>::BC - 1) / Tile<D>::BC;
+    const int n_kt = (a.N + Tile<D>::BC - 1) / Tile<D>::BC;
+    int kq = n_kt / n_splits, kr = n_kt % n_splits;
     const int bh_total = a.B * a.Hq;
     float c_log2 = fabsf(a.scale) * 1.4426950408889634f;
     // A zero scale makes every weight equal; a tiny positive factor gives the
@@ -580,9 +581,9 @@ hipError_t launch(const FwdArgs& a, int n_splits, float* op, float* lp, hipStrea
     __bf16* o = (__bf16*)a.o;
     float* lse = a.lse;
     void* args[] = {&q, &k, &v, &o, &lse, &group, &N, (void*)&n_qtiles, (void*)&bh_total,
-                    &c_log2, &qsign, &n_splits, &n_kt, &op, &lp};
+                    &c_log2, &qsign, &kq, &kr, &op, &lp};
     return hipLaunchKernel((const void*)fwd_bf16_kernel<D, CAUSAL, SPLIT>,
-                           dim3((SPLIT ? n_splits : 1) * bh_total * n_qtiles), dim3(kThreads), args, 0,
+                           dim3(bh_total * n_qtiles, SPLIT ? n_splits : 1), dim3(kThreads), args, 0,
                            stream);
 }
 
