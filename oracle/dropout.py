@@ -16,11 +16,17 @@ The readings taken here (each listed in the design notes):
   statistics m, l and the logsumexp are those of P before dropout.
 * Z comes from Philox4x32-10 (Salmon, Moraes, Dror and Shaw, "Parallel
   random numbers: as easy as 1, 2, 3", SC 2011), a counter-based generator:
-  the kept state is just (seed, offset).  For head unit bh = b * Hq + hq,
-  query row i and key j, the counter is (j // 4, i, bh, offset) and the key
-  (seed mod 2^32, seed // 2^32); output word j % 4 is the draw u_ij, and the
-  pair is kept iff u_ij >= t = floor(p * 2^32), p being the float32 value
-  the caller passes.  Then P(keep) = 1 - t / 2^32 = 1 - p exactly.
+  the kept state is just (seed, offset).  Each draw is 16 bits, so one
+  generator call (128 bits) serves eight keys of one query row.  For head
+  unit bh = b * Hq + hq, query row i and key j = 16a + 8b + 4c + w (b and c
+  in {0, 1}, w in 0..3), the draw u_ij is the 16-bit half number 4b + w,
+  counting from the low half of output word 0, of the call at counter
+  (2a + c, i, bh, offset) under the key (seed mod 2^32, seed // 2^32).  So
+  the call at counter (2a + c, ...) serves the keys 16a + 4c + {0..3} and
+  16a + 8 + 4c + {0..3}, in that order.  The pair is kept iff
+  u_ij >= t = floor(p * 2^16), p being the float32 value the caller passes:
+  P(keep) = 1 - t / 2^16, within 2^-16 of 1 - p.  Survivors are scaled by
+  1 / (1 - p).
 
 Gradients: with W = P (.) Z / (1 - p), O = W V, so
   dV = W^T dO,   dP = (dO V^T) (.) Z / (1 - p),
@@ -67,11 +73,11 @@ def philox4x32_10(c0, c1, c2, c3, k0, k1):
 
 
 def keep_threshold(p: float) -> int:
-    """t = floor(p * 2^32) for the float32 value of p (exact in fp64)."""
+    """t = floor(p * 2^16) for the float32 value of p (exact in fp64)."""
     p32 = float(np.float32(p))
     if not (0.0 <= p32 < 1.0):
         raise ValueError("dropout probability must be in [0, 1)")
-    return int(np.floor(p32 * 4294967296.0))
+    return int(np.floor(p32 * 65536.0))
 
 
 def keep_factor(p: float) -> float:
@@ -79,23 +85,31 @@ def keep_factor(p: float) -> float:
     return 1.0 / (1.0 - float(np.float32(p)))
 
 
+def draw_position(j):
+    """For key j = 16a + 8b + 4c + w: (counter word 0 = 2a + c, 16-bit half
+    index 4b + w of that call's output)."""
+    j = np.asarray(j, dtype=np.int64)
+    return 2 * (j >> 4) + ((j >> 2) & 1), 4 * ((j >> 3) & 1) + (j & 3)
+
+
 def dropout_draws(seed: int, offset: int, bh: int, rows, n_keys: int) -> np.ndarray:
-    """The 32-bit draws u_ij for the given query rows and keys 0..n_keys-1
-    of head unit bh: word j % 4 of Philox4x32-10 at counter
-    (j // 4, i, bh, offset) under key (seed mod 2^32, seed // 2^32).
-    Returns uint64 [len(rows), n_keys]."""
+    """The 16-bit draws u_ij for the given query rows and keys 0..n_keys-1
+    of head unit bh (module docstring).  Returns uint64 [len(rows), n_keys]."""
     rows = np.asarray(rows, dtype=np.int64).reshape(-1)
-    groups = (n_keys + 3) // 4
-    g = np.arange(groups, dtype=np.int64)[None, :]
-    i = rows[:, None]
+    n_ctr = 2 * ((n_keys + 15) // 16)
+    ctr = np.arange(n_ctr, dtype=np.int64)[None, :]
     seed = int(seed) & 0xFFFFFFFFFFFFFFFF
-    w = philox4x32_10(g, i, int(bh), int(offset), seed & 0xFFFFFFFF, seed >> 32)
-    out = np.stack(w, axis=-1).reshape(len(rows), 4 * groups)   # key 4g + word
-    return out[:, :n_keys]
+    words = philox4x32_10(ctr, rows[:, None], int(bh), int(offset), seed & 0xFFFFFFFF, seed >> 32)
+    halves = []
+    for wd in words:                      # half 2m is the low half of word m
+        halves += [wd & np.uint64(0xFFFF), wd >> np.uint64(16)]
+    halves = np.stack(halves, axis=-1)    # [R, n_ctr, 8]
+    c, hf = draw_position(np.arange(n_keys))
+    return halves[:, c, hf]
 
 
 def dropout_keep(seed: int, offset: int, bh: int, rows, n_keys: int, p: float) -> np.ndarray:
-    """Z_ij = [u_ij >= floor(p * 2^32)] as a bool array [len(rows), n_keys]."""
+    """Z_ij = [u_ij >= floor(p * 2^16)] as a bool array [len(rows), n_keys]."""
     return dropout_draws(seed, offset, bh, rows, n_keys) >= np.uint64(keep_threshold(p))
 
 

@@ -1,8 +1,8 @@
 """Pins of the dropout oracle (oracle/dropout.py) to things other than itself.
 
 * The generator: Philox4x32-10's published known-answer vectors
-  (tests/golden/philox4x32_10_kat.json), and the statistics a uniform 32-bit
-  generator must show (keep rate 1 - p, independent streams per head, offset
+  (tests/golden/philox4x32_10_kat.json), and the statistics uniform 16-bit
+  draws must show (keep rate 1 - p, independent streams per head, offset
   and seed).
 * The keep mask: each element is the draw of its own counter, checked one
   element at a time against single generator calls.
@@ -26,7 +26,8 @@ from oracle.attention import attention_head, masked_scores, softmax_rows
 from oracle.backward import attention_backward_head
 from oracle.dropout import (attention_dropout_backward_head, attention_dropout_backward_ref,
                             attention_dropout_head, attention_dropout_ref, attention_dropout_rows,
-                            dropout_draws, dropout_keep, keep_factor, keep_threshold, philox4x32_10)
+                            draw_position, dropout_draws, dropout_keep, keep_factor, keep_threshold,
+                            philox4x32_10)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "philox4x32_10_kat.json")
 
@@ -61,33 +62,51 @@ def test_philox_vectorised_equals_elementwise():
 
 def test_threshold_and_factor():
     assert keep_threshold(0.0) == 0
-    assert keep_threshold(0.5) == 2**31
-    assert keep_threshold(0.25) == 2**30
+    assert keep_threshold(0.5) == 2**15
+    assert keep_threshold(0.25) == 2**14
     p32 = float(np.float32(0.1))
-    assert keep_threshold(0.1) == int(np.floor(p32 * 2**32))
+    assert keep_threshold(0.1) == int(np.floor(p32 * 2**16)) == 6553
     assert keep_factor(0.5) == 2.0
     for bad in (-0.1, 1.0, 1.5, float("nan")):
         with pytest.raises(ValueError):
             keep_threshold(bad)
 
 
+def test_draw_positions_cover_each_call_once():
+    """Every call (counter) serves exactly eight keys, one per 16-bit half:
+    keys 16a + 4c + {0..3} and 16a + 8 + 4c + {0..3}, in that order."""
+    j = np.arange(64)
+    c, hf = draw_position(j)
+    for ctr in range(8):
+        keys = j[c == ctr]
+        a, cc = ctr // 2, ctr % 2
+        want = [16 * a + 4 * cc + w for w in range(4)] + [16 * a + 8 + 4 * cc + w for w in range(4)]
+        assert list(keys) == want
+        assert list(hf[c == ctr]) == list(range(8))
+
+
 # ---- pins of the keep mask -----------------------------------------------------
 
 def pin_keep_elementwise(keep):
-    """Each Z_ij is [word j % 4 of Philox(j // 4, i, bh, offset; seed) >= t]."""
+    """Each Z_ij is [u_ij >= t] with u_ij the 16-bit half 4b + w of the call
+    at counter (2a + c, i, bh, offset), for j = 16a + 8b + 4c + w."""
     rng = np.random.default_rng(2)
     for seed, offset, bh, p in [(0, 0, 0, 0.5), (2**40 + 77, 3, 5, 0.1), (123456789, 9, 1000, 0.9)]:
-        z = keep(seed, offset, bh, np.arange(40), 23, p)
+        z = keep(seed, offset, bh, np.arange(40), 45, p)
         t = keep_threshold(p)
-        for _ in range(60):
-            i, j = int(rng.integers(0, 40)), int(rng.integers(0, 23))
-            w = philox4x32_10(j // 4, i, bh, offset, seed & 0xFFFFFFFF, seed >> 32)[j % 4]
-            assert bool(z[i, j]) == (int(w) >= t), (seed, offset, bh, i, j)
+        for _ in range(80):
+            i, j = int(rng.integers(0, 40)), int(rng.integers(0, 45))
+            a, b, c, w = j // 16, (j // 8) % 2, (j // 4) % 2, j % 4
+            half = 4 * b + w
+            word = philox4x32_10(2 * a + c, i, bh, offset, seed & 0xFFFFFFFF, seed >> 32)[half // 2]
+            u = (int(word) >> (16 * (half % 2))) & 0xFFFF
+            assert bool(z[i, j]) == (u >= t), (seed, offset, bh, i, j)
 
 
 def pin_keep_rate(keep):
-    """A uniform 32-bit draw passes u >= floor(p 2^32) with probability 1 - p:
-    the kept fraction of 65536 draws is within 5 sigma of it."""
+    """A uniform 16-bit draw passes u >= floor(p 2^16) with probability
+    within 2^-16 of 1 - p: the kept fraction of 65536 draws is within
+    5 sigma of it."""
     for p in (0.1, 0.5, 0.9):
         z = keep(7, 1, 3, np.arange(256), 256, p)
         n = z.size
@@ -105,12 +124,14 @@ def pin_streams_independent(keep):
 
 
 def test_draws_are_uniform():
-    """The top 4 bits of 2^16 draws fill 16 bins evenly (chi-square, 15
-    degrees of freedom, far below the 0.1% point 37.7)."""
+    """The top 4 bits of 2^16 16-bit draws fill 16 bins evenly (chi-square,
+    15 degrees of freedom, below the 0.1% point 37.7), and so do the low 4."""
     u = dropout_draws(5, 2, 9, np.arange(256), 256)
-    hist = np.bincount((u >> np.uint64(28)).astype(np.int64).ravel(), minlength=16)
-    e = u.size / 16
-    assert np.sum((hist - e) ** 2 / e) < 37.7
+    assert int(u.max()) < 2**16
+    for bits in (u >> np.uint64(12), u & np.uint64(15)):
+        hist = np.bincount(bits.astype(np.int64).ravel(), minlength=16)
+        e = u.size / 16
+        assert np.sum((hist - e) ** 2 / e) < 37.7
 
 
 # ---- pins of the forward -------------------------------------------------------
@@ -267,16 +288,28 @@ def test_backward_gqa_group_sums():
 
 # ---- planted mistakes ------------------------------------------------------------
 
-def _keep_mutant(inverted=False, reversed_words=False, swapped_fields=False, ignore_bh=False):
+def _keep_mutant(inverted=False, halves_swapped=False, swapped_fields=False, ignore_bh=False,
+                 plain_order=False):
     def keep(seed, offset, bh, rows, n_keys, p):
         rows = np.asarray(rows).reshape(-1)
-        g = np.arange((n_keys + 3) // 4)[None, :]
+        n_ctr = 2 * ((n_keys + 15) // 16)
+        ctr = np.arange(n_ctr)[None, :]
         i = rows[:, None]
-        c0, c1 = (i, g) if swapped_fields else (g, i)
+        c0, c1 = (i, ctr) if swapped_fields else (ctr, i)
         w = philox4x32_10(c0, c1, 0 if ignore_bh else bh, offset, seed & 0xFFFFFFFF, seed >> 32)
-        if reversed_words:
-            w = w[::-1]
-        u = np.stack(np.broadcast_arrays(*w), axis=-1).reshape(len(rows), -1)[:, :n_keys]
+        halves = []
+        for wd in np.broadcast_arrays(*w):
+            lo, hi = wd & np.uint64(0xFFFF), wd >> np.uint64(16)
+            halves += [hi, lo] if halves_swapped else [lo, hi]
+        halves = np.stack(halves, axis=-1)
+        if swapped_fields:
+            halves = np.swapaxes(halves, 0, 1)
+        j = np.arange(n_keys)
+        if plain_order:                  # keys 8n..8n+7 on call n
+            c, hf = j // 8, j % 8
+        else:
+            c, hf = draw_position(j)
+        u = halves[:, c, hf]
         t = np.uint64(keep_threshold(p))
         return u < t if inverted else u >= t
     return keep
@@ -318,9 +351,10 @@ def _bwd_mutant(no_dp_mask=False, dv_from_p=False, d_from_undropped=False):
 
 KEEP_MUTANTS = {
     "comparison inverted": _keep_mutant(inverted=True),
-    "word order reversed": _keep_mutant(reversed_words=True),
+    "16-bit halves swapped": _keep_mutant(halves_swapped=True),
     "counter fields swapped": _keep_mutant(swapped_fields=True),
     "head unit ignored": _keep_mutant(ignore_bh=True),
+    "keys in plain order on the calls": _keep_mutant(plain_order=True),
 }
 FWD_MUTANTS = {
     "1/(1-p) left out": _fwd_mutant(no_factor=True),
