@@ -144,6 +144,8 @@ def main() -> int:
     ap.add_argument("--splitkv", type=int, default=0,
                     help="time fa_fwd_splitkv with this many splits (and fa_fwd beside it)")
     ap.add_argument("--backward", action="store_true", help="time the backward pass (fa_bwd)")
+    ap.add_argument("--dropout", type=float, default=0.0,
+                    help="time fa_fwd_dropout with this drop probability (and fa_fwd beside it)")
     args = ap.parse_args()
 
     if args.summarize:
@@ -164,6 +166,8 @@ def main() -> int:
 
     if args.splitkv:
         return bench_splitkv(args)
+    if args.dropout:
+        return bench_dropout(args)
     if args.backward:
         return bench_backward(args)
     w = CONFIGS[args.config or "c3"]
@@ -357,6 +361,78 @@ def bench_splitkv(args) -> int:
         "merge_algorithmic_bytes": merge_bytes,
         "parity": {"rows": len(rows), "max_abs_o": float(err.max()),
                    "mean_abs_o": float(err.mean()), "max_abs_lse": float(lerr.max()), "ok": ok},
+    }
+    print(json.dumps(out), flush=True)
+    return 0 if ok else 1
+
+
+def bench_dropout(args) -> int:
+    """fa_fwd_dropout against fa_fwd on the same resident inputs (default
+    c3); one JSON line.  FLOPs are the nominal forward count: dropout adds
+    generator and integer work, not matrix work.  Parity: sampled rows
+    against the oracle's dropout forward."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from io_aware_tiled_04_amd import fa
+    from io_aware_tiled_04_amd.workloads import CONFIGS, EXTRA, as_f64_numpy, make_inputs
+
+    name = args.config or "c3"
+    w = EXTRA.get(name) or CONFIGS[name]
+    p, seed, offset = float(args.dropout), 0x5EED5EED12345678, 1
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q, k, v = make_inputs(w)
+    qd, kd, vd = (t.to(dev) for t in (q, k, v))
+    o = torch.empty_like(qd)
+    lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    ptrs = (qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(), lse.data_ptr())
+
+    def launch_direct():
+        rc = fa.fa_fwd(*ptrs, w.B, w.Hq, w.Hkv, w.N, w.d, int(w.causal), w.scale, stream.cuda_stream)
+        if rc != fa.FA_OK:
+            raise fa.FaError(rc)
+
+    def launch_drop():
+        rc = fa.fa_fwd_dropout(*ptrs, w.B, w.Hq, w.Hkv, w.N, w.d, int(w.causal), w.scale, p, seed,
+                               offset, stream.cuda_stream)
+        if rc != fa.FA_OK:
+            raise fa.FaError(rc)
+
+    direct_ms, _ = _time_launches(launch_direct, stream, args.steps, args.warmup)
+    drop_ms, drop_total = _time_launches(launch_drop, stream, args.steps, args.warmup)
+
+    rng = np.random.default_rng(0)
+    rows = [(0, 0, 0), (w.B - 1, w.Hq - 1, w.N - 1)] + [
+        (int(rng.integers(0, w.B)), int(rng.integers(0, w.Hq)), int(rng.integers(0, w.N))) for _ in range(30)]
+    o_ref, lse_ref = oracle.attention_dropout_rows(as_f64_numpy(q), as_f64_numpy(k), as_f64_numpy(v),
+                                                   w.causal, w.scale, p, seed, offset, rows)
+    idx = tuple(np.array(rows).T)
+    err = np.abs(as_f64_numpy(o)[idx] - o_ref)
+    excess = err - 2.0 ** -8 * np.abs(o_ref)
+    lerr = np.abs(as_f64_numpy(lse)[idx] - lse_ref)
+    factor = 1.0 / (1.0 - float(np.float32(p)))
+    ok = bool(excess.max() <= 2e-2 and err.mean() <= 2e-3 * factor and lerr.max() <= 1e-3)
+    flops = w.nominal_flops()
+    out = {
+        "metric": "attention fwd TFLOP/s with dropout on the weights (bf16)",
+        "value": round(flops * args.steps / (drop_total * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(drop_total / args.steps, 5), "higher_is_better": True,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{w.name}: {w.note}", "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N,
+                   "d": w.d, "causal": w.causal, "seed": w.seed, "p_drop": p,
+                   "flops_per_step": flops},
+        "kernel": f"fwd_bf16_kernel<{w.d}, {'causal' if w.causal else 'full'}, dropout>",
+        "dropout_avg_launch_us": round(drop_ms * 1e3, 2),
+        "direct_avg_launch_us": round(direct_ms * 1e3, 2),
+        "dropout_tflops_per_launch": round(flops / (drop_ms * 1e-3) / 1e12, 2),
+        "direct_tflops_per_launch": round(flops / (direct_ms * 1e-3) / 1e12, 2),
+        "slowdown_vs_direct": round(drop_ms / direct_ms, 3),
+        "parity": {"rows": len(rows), "max_abs_o": float(err.max()), "mean_abs_o": float(err.mean()),
+                   "max_abs_lse": float(lerr.max()), "ok": ok},
     }
     print(json.dumps(out), flush=True)
     return 0 if ok else 1

@@ -61,7 +61,7 @@ enum fa_status {
     FA_ERR_SHAPE = -2,     /* B, Hq, Hkv or N <= 0, or the problem is too large to index */
     FA_ERR_HEADS = -3,     /* Hq is not a multiple of Hkv */
     FA_ERR_HEADDIM = -4,   /* d is not one of the supported head sizes (64, 128) */
-    FA_ERR_ARG = -5,       /* scale is not finite, or num_splits is out of range */
+    FA_ERR_ARG = -5,       /* scale is not finite, num_splits or p_drop is out of range */
     FA_ERR_HIP = -6,       /* the HIP runtime rejected the launch */
     FA_ERR_WORKSPACE = -7  /* a workspace argument is null or too small */
 };
@@ -133,6 +133,37 @@ size_t fa_fwd_splitkv_workspace_size(int B, int Hq, int N, int d, int num_splits
 int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
                    int B, int Hq, int Hkv, int N, int d, int causal, float scale,
                    int num_splits, void* workspace, size_t workspace_bytes,
+                   hipStream_t stream);
+
+/*
+ * fa_fwd_dropout - fa_fwd with dropout on the attention weights.
+ *
+ * The reading-notes page (section 其他算子) has dropout set attention weights
+ * to zero at random with probability p and keep the random generator's
+ * state for the backward pass.  Here:
+ *   O   = (P (.) Z) V / (1 - p_drop),   LSE as for fa_fwd (before dropout),
+ * with P the softmax weights of fa_fwd and Z_ij in {0, 1} drawn by
+ * Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC 2011), a counter-based
+ * generator, so the whole state is (seed, offset):
+ *   for head unit bh = b * Hq + hq, query row i and key
+ *   j = 16a + 8b + 4c + w (b, c in {0, 1}, w in 0..3), the draw u_ij is the
+ *   16-bit half number 4b + w (low half of output word 0 first) of the call
+ *   at counter (2a + c, i, bh, offset) with key (seed mod 2^32, seed >> 32);
+ *   Z_ij = 1 iff u_ij >= floor(p_drop * 2^16).
+ * The keep probability is thus within 2^-16 of 1 - p_drop.  Passing the
+ * same (seed, offset) to another call draws the same Z.
+ *
+ * Arguments q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, stream: as for
+ *   fa_fwd.
+ * p_drop: the drop probability, 0 <= p_drop < 1 (FA_ERR_ARG otherwise).
+ *   p_drop = 0 gives exactly fa_fwd's result.
+ * seed: 64-bit generator key.  offset: 32-bit stream number; calls with one
+ *   seed that must draw independent masks use different offsets.
+ * Returns FA_OK or a negative fa_status.
+ */
+int fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                   float p_drop, unsigned long long seed, unsigned int offset,
                    hipStream_t stream);
 
 /*

@@ -68,6 +68,36 @@ extern "C" int fa_fwd_f32(const float* q, const float* k, const float* v, float*
 
 namespace {
 
+// Dropout parameters: 0 <= p < 1; t = floor(p * 2^16) (exact in double).
+int make_dropout(float p, unsigned long long seed, unsigned int offset, fa::Dropout* dr) {
+    if (!(p >= 0.f && p < 1.f)) return FA_ERR_ARG;
+    const uint32_t t = (uint32_t)std::floor((double)p * 65536.0);
+    dr->k0 = (uint32_t)(seed & 0xFFFFFFFFull);
+    dr->k1 = (uint32_t)(seed >> 32);
+    dr->offset = offset;
+    dr->t2 = t | (t << 16);
+    dr->factor = 1.f / (1.f - p);
+    return FA_OK;
+}
+
+}  // namespace
+
+extern "C" int fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                              int Hq, int Hkv, int N, int d, int causal, float scale, float p_drop,
+                              unsigned long long seed, unsigned int offset, hipStream_t stream) {
+    int rc = validate(q, k, v, o, lse, B, Hq, Hkv, N, d, scale);
+    if (rc != FA_OK) return rc;
+    fa::Dropout dr;
+    rc = make_dropout(p_drop, seed, offset, &dr);
+    if (rc != FA_OK) return rc;
+    const fa::FwdArgs a = pack(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale);
+    // p = 0 keeps every weight with factor 1: the plain kernel computes exactly that.
+    const hipError_t e = p_drop == 0.f ? fa::launch_fwd_bf16(a, stream) : fa::launch_fwd_bf16_dropout(a, dr, stream);
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+namespace {
+
 // Split count and workspace checks of the split-KV entry point (after the
 // common validation).
 int validate_split(int B, int Hq, int N, int d, int num_splits, const void* workspace,
@@ -150,7 +180,7 @@ extern "C" const char* fa_status_string(int status) {
         case FA_ERR_SHAPE: return "invalid shape (B, Hq, Hkv and N must be positive and the problem indexable)";
         case FA_ERR_HEADS: return "Hq must be a multiple of Hkv";
         case FA_ERR_HEADDIM: return "unsupported head size d (supported: 64, 128)";
-        case FA_ERR_ARG: return "invalid scalar argument (scale must be finite, num_splits in 1..256)";
+        case FA_ERR_ARG: return "invalid scalar argument (scale must be finite, num_splits in 1..256, p_drop in [0, 1))";
         case FA_ERR_WORKSPACE: return "workspace is null or smaller than the size the entry point needs";
         case FA_ERR_HIP: return "HIP launch failed";
         default: return "unknown status";

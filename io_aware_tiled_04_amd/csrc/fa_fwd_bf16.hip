@@ -59,6 +59,8 @@
 
 #include <stdint.h>
 
+#include "philox.h"
+
 namespace fa {
 namespace {
 
@@ -200,6 +202,11 @@ __device__ __forceinline__ void store_vt(LDS char* buf, int gt, const Stage<D>& 
 // their use (scheduling groups below), so the LDS latency stays hidden
 // behind the matrix core instead of stalling every MFMA.
 constexpr int kAhead = 4;
+
+template <bool B>
+struct MaskTag {
+    static constexpr bool value = B;
+};
 constexpr int kSchedMfma = 0x008;
 constexpr int kSchedDsRead = 0x100;
 
@@ -270,6 +277,30 @@ __device__ __forceinline__ float exp_tile(const f32x16 (&s)[Tile<D>::KB], bf16x8
     return (ps[0] + ps[1]) + (ps[2] + ps[3]);
 }
 
+// Dropout on the bf16 weights of one tile (the row sum has already taken
+// them whole): pb[s] holds this lane's keys key0 + 16s + 4h + {0..3, 8..11}
+// of query row `row` in the order of the generator's 16-bit halves, so the
+// call at counter (2 (key0/16 + s) + h, row, bh, offset) decides, word by
+// word, the four packed pairs of pb[s].
+template <int D>
+__device__ __forceinline__ void apply_dropout(bf16x8 (&pb)[Tile<D>::BC / 16], int key0, int row, int bh,
+                                              const Dropout& dr, int h) {
+    // The first rounds depend only on the row, the head and the offset; the
+    // empty asm hides that from the optimiser, which would otherwise keep
+    // those partial states live across the whole key loop (and spill them).
+    uint32_t row_u = (uint32_t)row;
+    asm volatile("" : "+v"(row_u));
+#pragma unroll
+    for (int s = 0; s < Tile<D>::BC / 16; ++s) {
+        const PhiloxOut r = philox4x32_10((uint32_t)(2 * ((key0 >> 4) + s) + h), row_u, (uint32_t)bh,
+                                          dr.offset, dr.k0, dr.k1);
+        u32x4 x = __builtin_bit_cast(u32x4, pb[s]);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) x[m] = drop_pair(x[m], r.w[m], dr.t2);
+        pb[s] = __builtin_bit_cast(bf16x8, x);
+    }
+}
+
 // Online softmax of one tile of S^T: mask, P against the reference max m,
 // row sum.  The reference max is lazy: after the first tile it only moves
 // when some p of the wave would exceed kSumLimit (detected through the row
@@ -286,13 +317,16 @@ __device__ __forceinline__ void softmax_tile(f32x16 (&s)[Tile<D>::KB], bf16x8 (&
     const int h = lane >> 5;
 
     if constexpr (MASK) {
+        // Register i of block kb holds key key0 + 4h + off with
+        // off = 32 kb + 8 (i / 4) + i % 4; the key is dead (past N, or after
+        // the query when causal) iff off >= lim.  One limit per tile keeps
+        // the offsets immediate.
+        const int lim = (CAUSAL ? min(N, my_row + 1) : N) - key0 - 4 * h;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const int key = key0 + 32 * kb + 8 * (i >> 2) + 4 * h + (i & 3);
-                const bool dead = key >= N || (CAUSAL && key > my_row);
-                if (dead) s[kb][i] = -__builtin_inff();
+                if (32 * kb + 8 * (i >> 2) + (i & 3) >= lim) s[kb][i] = -__builtin_inff();
             }
         }
     }
@@ -336,11 +370,17 @@ __device__ __forceinline__ void softmax_tile(f32x16 (&s)[Tile<D>::KB], bf16x8 (&
 // of its range instead of O and LSE: the output normalised by its own row
 // sum to OP[s][bh][row][d], and the logsumexp of its range to LP[s][bh][row]
 // (O = 0 and LSE = -inf for a row that sees no key of the range).
-template <int D, bool CAUSAL, bool SPLIT>
+//
+// DROP (never with SPLIT): dropout with the parameters `dr` on the weights
+// that enter P V; the row sums, hence the logsumexp, take the weights whole,
+// and the epilogue multiplies O by 1 / (1 - p).
+template <int D, bool CAUSAL, bool SPLIT, bool DROP>
 __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     __bf16* __restrict__ O, float* __restrict__ LSE, int group, int N, int n_qtiles, int bh_total,
-    float c_log2, uint32_t qsign, int kq, int kr, float* __restrict__ OP, float* __restrict__ LP) {
+    float c_log2, uint32_t qsign, int kq, int kr, float* __restrict__ OP, float* __restrict__ LP,
+    Dropout dr) {
+    static_assert(!(SPLIT && DROP), "dropout runs on the direct path only");
     using T = Tile<D>;
     constexpr int BC = T::BC;
     constexpr int KB = T::KB;
@@ -496,27 +536,30 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
             gemm_phase<D, false, true>(vl, kl, pb, qf, oacc, s, lane);
         __builtin_amdgcn_s_setprio(0);
     };
-    auto softmax_phase = [&](int t) __attribute__((always_inline)) {
+    // MASKED: the tile may hold dead keys (past N, or after some query of
+    // the workgroup when causal); the masked softmax is exact on any tile.
+    auto softmax_phase = [&](auto masked, int t) __attribute__((always_inline)) {
         if (t >= 0 && t < w_tiles) {
             const int key0 = (kt_lo + t) * BC;
-            if ((key0 + BC > N) || (CAUSAL && key0 + BC - 1 > wq0))
-                softmax_tile<D, CAUSAL, true>(s, pb, oacc, m_run, l_run, key0, N, my_row, c_log2, lane, t == 0);
-            else
-                softmax_tile<D, CAUSAL, false>(s, pb, oacc, m_run, l_run, key0, N, my_row, c_log2, lane, t == 0);
+            softmax_tile<D, CAUSAL, decltype(masked)::value>(s, pb, oacc, m_run, l_run, key0, N, my_row,
+                                                             c_log2, lane, t == 0);
+            // Dropout thins the weights that enter P V; the row sum above
+            // took them whole.
+            if constexpr (DROP) apply_dropout<D>(pb, key0, my_row, bh, dr, h);
         }
     };
     // Phases 2u and 2u+1.
-    auto tile_pair = [&](int u) __attribute__((always_inline)) {
+    auto tile_pair = [&](auto masked, int u) __attribute__((always_inline)) {
         if (grp == 0) {
             load_v<D>(vg, min(u, n_tiles - 1) * BC, Nl, gt, stg);
             matrix_phase(u);
         } else {            // vector phase of tile u-1 of the second group
-            softmax_phase(u - 1);
+            softmax_phase(masked, u - 1);
             if (u + 1 < n_tiles) store_k<D>(smem + ((u + 1) & 1 ? T::K1 : T::K0), gt, stg);
         }
         __syncthreads();
         if (grp == 0) {     // vector phase of tile u of the first group
-            softmax_phase(u);
+            softmax_phase(masked, u);
             if (u < n_tiles) store_vt<D>(smem + (u & 1 ? T::V1 : T::V0), gt, stg);
         } else {
             load_k<D>(kg, min(u + 2, n_tiles - 1) * BC, Nl, gt, stg);
@@ -524,8 +567,19 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
         }
         __syncthreads();
     };
+    // Local tile t holds keys from (kt_lo + t) BC on.  No key of a tile
+    // before t_mask is dead for any row of the workgroup: the tail starts at
+    // tile N / BC, and when causal the first row q0 sees every key of tiles
+    // below q0 / BC (q0 is a multiple of BC).  The pair loop switches to the
+    // masked softmax at the first pair that can run such a tile.
+    int t_mask = N / BC - kt_lo;
+    if (CAUSAL) t_mask = min(t_mask, q0 / BC - kt_lo);
+    t_mask = max(0, min(t_mask, n_tiles + 1));
+    int u = 0;
 #pragma unroll 1
-    for (int u = 0; u <= n_tiles; ++u) tile_pair(u);
+    for (; u < t_mask; ++u) tile_pair(MaskTag<false>{}, u);
+#pragma unroll 1
+    for (; u <= n_tiles; ++u) tile_pair(MaskTag<true>{}, u);
 
     if (wq0 >= N) return;
     const float l_tot = half_swap_sum(l_run);
@@ -546,7 +600,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
             LP[prow] = seen ? (m_run + __builtin_log2f(l_tot)) * 0.69314718055994531f : -__builtin_inff();
         return;
     }
-    const float inv = 1.f / l_tot;
+    const float inv = DROP ? dr.factor / l_tot : 1.f / l_tot;
     __bf16* op = O + q_head + (size_t)my_row * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
@@ -561,8 +615,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     if (h == 0) LSE[(size_t)bh * N + my_row] = (m_run + __builtin_log2f(l_tot)) * 0.69314718055994531f;
 }
 
-template <int D, bool CAUSAL, bool SPLIT>
-hipError_t launch(const FwdArgs& a, int n_splits, float* op, float* lp, hipStream_t stream) {
+template <int D, bool CAUSAL, bool SPLIT, bool DROP = false>
+hipError_t launch(const FwdArgs& a, int n_splits, float* op, float* lp, hipStream_t stream,
+                  Dropout dr = Dropout{}) {
     const int n_qtiles = (a.N + kBr - 1) / kBr;
     const int n_kt = (a.N + Tile<D>::BC - 1) / Tile<D>::BC;
     int kq = n_kt / n_splits, kr = n_kt % n_splits;
@@ -581,8 +636,8 @@ hipError_t launch(const FwdArgs& a, int n_splits, float* op, float* lp, hipStrea
     __bf16* o = (__bf16*)a.o;
     float* lse = a.lse;
     void* args[] = {&q, &k, &v, &o, &lse, &group, &N, (void*)&n_qtiles, (void*)&bh_total,
-                    &c_log2, &qsign, &kq, &kr, &op, &lp};
-    return hipLaunchKernel((const void*)fwd_bf16_kernel<D, CAUSAL, SPLIT>,
+                    &c_log2, &qsign, &kq, &kr, &op, &lp, &dr};
+    return hipLaunchKernel((const void*)fwd_bf16_kernel<D, CAUSAL, SPLIT, DROP>,
                            dim3(bh_total * n_qtiles, SPLIT ? n_splits : 1), dim3(kThreads), args, 0,
                            stream);
 }
@@ -645,6 +700,14 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
                         : launch<128, false, false>(a, 1, nullptr, nullptr, stream);
     return a.causal ? launch<64, true, false>(a, 1, nullptr, nullptr, stream)
                     : launch<64, false, false>(a, 1, nullptr, nullptr, stream);
+}
+
+hipError_t launch_fwd_bf16_dropout(const FwdArgs& a, const Dropout& dr, hipStream_t stream) {
+    if (a.d == 128)
+        return a.causal ? launch<128, true, false, true>(a, 1, nullptr, nullptr, stream, dr)
+                        : launch<128, false, false, true>(a, 1, nullptr, nullptr, stream, dr);
+    return a.causal ? launch<64, true, false, true>(a, 1, nullptr, nullptr, stream, dr)
+                    : launch<64, false, false, true>(a, 1, nullptr, nullptr, stream, dr);
 }
 
 hipError_t launch_fwd_bf16_split(const FwdArgs& a, int n_splits, float* workspace, hipStream_t stream) {

@@ -2,6 +2,7 @@
 // Arguments are validated by the caller (fa_api.cpp) before these run.
 #pragma once
 #include <hip/hip_runtime.h>
+#include <stdint.h>
 
 namespace fa {
 
@@ -32,12 +33,26 @@ struct BwdArgs {
     float scale;
 };
 
+// Dropout on the attention weights: the Philox4x32-10 key (the seed), the
+// call offset, the keep threshold t = floor(p * 2^16) in both 16-bit halves
+// of t2, and the survivors' factor 1 / (1 - p).  The draws are defined in
+// philox.h.
+struct Dropout {
+    uint32_t k0, k1;   // seed mod 2^32, seed >> 32
+    uint32_t offset;
+    uint32_t t2;       // t | t << 16
+    float factor;      // 1 / (1 - p)
+};
+
 // Each returns hipSuccess or the launch error.
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
 // Split-KV form of launch_fwd_bf16: partials of n_splits key ranges into
 // `workspace` (float32, split_workspace_floats(...) elements), then a merge
 // into a.o and a.lse.  Both kernels are enqueued on `stream`.
 hipError_t launch_fwd_bf16_split(const FwdArgs& a, int n_splits, float* workspace, hipStream_t stream);
+// launch_fwd_bf16 with dropout on the weights (the logsumexp is that of the
+// weights before dropout).
+hipError_t launch_fwd_bf16_dropout(const FwdArgs& a, const Dropout& dr, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
 // Backward pass: D = rowsum(dO * O) into `workspace` (B*Hq*N floats), then
 // the dQ, dK and dV kernels, all enqueued on `stream`.

@@ -4,12 +4,11 @@ Only argument marshalling lives here: every step of the forward pass runs in
 the HIP kernels of ``libfa.so``.  There is no fallback: if the library is
 missing or cannot be loaded, importing this module raises.
 
-``fa_fwd``, ``fa_fwd_f32``, ``fa_fwd_splitkv``,
-``fa_fwd_splitkv_workspace_size`` and ``fa_status_string`` have the C names
-and arguments (integer device pointers, sizes, stream handle).  ``fwd`` and
-``fwd_splitkv`` are the torch-facing conveniences: they check the tensors,
-allocate O, LSE (and the split-KV workspace) on the inputs' device and launch
-on torch's current stream.
+The ``fa_*`` functions have the C names and arguments (integer device
+pointers, sizes, stream handle).  ``fwd``, ``fwd_splitkv``, ``fwd_dropout``
+and ``bwd`` are the torch-facing conveniences: they check the tensors,
+allocate the outputs (and any workspace) on the inputs' device and launch on
+torch's current stream.
 """
 from __future__ import annotations
 
@@ -31,7 +30,7 @@ FA_ERR_WORKSPACE = -7
 
 # Names declared in include/fa.h, in order.
 EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_fwd_splitkv_workspace_size", "fa_fwd_splitkv",
-           "fa_bwd_workspace_size", "fa_bwd", "fa_status_string")
+           "fa_fwd_dropout", "fa_bwd_workspace_size", "fa_bwd", "fa_status_string")
 
 
 def _load():
@@ -48,6 +47,9 @@ def _load():
     lib.fa_fwd_splitkv.argtypes = fwd_args[:-1] + [ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t,
                                                    ctypes.c_void_p]
     lib.fa_fwd_splitkv.restype = ctypes.c_int
+    lib.fa_fwd_dropout.argtypes = fwd_args[:-1] + [ctypes.c_float, ctypes.c_ulonglong, ctypes.c_uint,
+                                                   ctypes.c_void_p]
+    lib.fa_fwd_dropout.restype = ctypes.c_int
     lib.fa_fwd_splitkv_workspace_size.argtypes = [ctypes.c_int] * 5
     lib.fa_fwd_splitkv_workspace_size.restype = ctypes.c_size_t
     lib.fa_bwd.argtypes = [ctypes.c_void_p] * 9 + [ctypes.c_int] * 6 + \
@@ -93,6 +95,14 @@ def fa_fwd_splitkv(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, num_splits,
     """Raw call of the split-KV C entry point; pointers and stream are integers."""
     return _lib.fa_fwd_splitkv(q, k, v, o, lse, B, Hq, Hkv, N, d, int(causal), float(scale),
                                int(num_splits), workspace, int(workspace_bytes), stream)
+
+
+def fa_fwd_dropout(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, p_drop, seed, offset,
+                   stream) -> int:
+    """Raw call of the dropout C entry point; pointers and stream are integers."""
+    return _lib.fa_fwd_dropout(q, k, v, o, lse, B, Hq, Hkv, N, d, int(causal), float(scale),
+                               float(p_drop), int(seed) & 0xFFFFFFFFFFFFFFFF,
+                               int(offset) & 0xFFFFFFFF, stream)
 
 
 def fa_bwd_workspace_size(B, Hq, N) -> int:
@@ -192,6 +202,33 @@ def fwd_splitkv(q, k, v, num_splits: int, causal: bool = False, scale: float | N
     if rc != FA_OK:
         raise FaError(rc)
     return o, lse
+
+
+def fwd_dropout(q, k, v, p_drop: float, seed: int, offset: int = 0, causal: bool = False,
+                scale: float | None = None, stream=None):
+    """Attention forward with dropout on the weights, on bf16 tensors:
+    returns (O, LSE, (seed, offset)).  The last item is the generator state
+    that regenerates the same keep mask (the entry point draws it from
+    Philox4x32-10 at that seed and offset).  LSE is that of the weights
+    before dropout.  Launches on ``stream`` or torch's current stream."""
+    import torch
+    dev = q.device
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, n, torch.bfloat16, dev)
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    if tuple(k.shape) != (B, Hkv, N, d) or tuple(v.shape) != (B, Hkv, N, d):
+        raise ValueError("k and v must be [B, Hkv, N, d] with q's B, N and d")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
+    s = (stream if stream is not None else torch.cuda.current_stream(dev)).cuda_stream
+    rc = fa_fwd_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                        B, Hq, Hkv, N, d, causal, scale, p_drop, seed, offset, s)
+    if rc != FA_OK:
+        raise FaError(rc)
+    return o, lse, (int(seed) & 0xFFFFFFFFFFFFFFFF, int(offset) & 0xFFFFFFFF)
 
 
 def bwd(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None, workspace=None,

@@ -21,7 +21,7 @@ def _declared():
 
 def test_header_declares_the_entry_points():
     assert _declared() == ["fa_fwd", "fa_fwd_f32", "fa_fwd_splitkv_workspace_size",
-                           "fa_fwd_splitkv", "fa_bwd_workspace_size", "fa_bwd",
+                           "fa_fwd_splitkv", "fa_fwd_dropout", "fa_bwd_workspace_size", "fa_bwd",
                            "fa_status_string"]
 
 
@@ -112,6 +112,29 @@ def test_splitkv_workspace_size():
     for bad in [(0, 4, 300, 64, 2), (1, 0, 300, 64, 2), (1, 4, 0, 64, 2), (1, 4, 300, 96, 2),
                 (1, 4, 300, 64, 0), (1, 4, 300, 64, 257)]:
         assert fa.fa_fwd_splitkv_workspace_size(*bad) == 0, bad
+
+
+def test_dropout_rejects_invalid_arguments():
+    """The dropout entry point runs fa_fwd's validation, then checks p_drop
+    (0 <= p < 1, finite)."""
+    from io_aware_tiled_04_amd import fa
+    base = (P, P, P, P, P, 1, 2, 1, 128, 64, 1, 0.125)
+    cases = [
+        ((0,) + base[1:], 0.1, "FA_ERR_NULL"),
+        (base[:4] + (0,) + base[5:], 0.1, "FA_ERR_NULL"),
+        (base[:8] + (0,) + base[9:], 0.1, "FA_ERR_SHAPE"),
+        (base[:5] + (1, 3, 2) + base[8:], 0.1, "FA_ERR_HEADS"),
+        (base[:9] + (96,) + base[10:], 0.1, "FA_ERR_HEADDIM"),
+        (base[:11] + (math.nan,), 0.1, "FA_ERR_ARG"),
+        (base, -0.01, "FA_ERR_ARG"),
+        (base, 1.0, "FA_ERR_ARG"),
+        (base, 1.5, "FA_ERR_ARG"),
+        (base, math.nan, "FA_ERR_ARG"),
+        (base, math.inf, "FA_ERR_ARG"),
+    ]
+    for args, p, expect in cases:
+        rc = fa.fa_fwd_dropout(*args, p, 7, 0, 0)
+        assert rc == getattr(fa, expect), (args, p, rc, fa.fa_status_string(rc))
 
 
 @pytest.mark.parametrize("ptrs,sizes,ws,expect", [
