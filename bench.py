@@ -166,10 +166,10 @@ def main() -> int:
 
     if args.splitkv:
         return bench_splitkv(args)
-    if args.dropout:
-        return bench_dropout(args)
     if args.backward:
         return bench_backward(args)
+    if args.dropout:
+        return bench_dropout(args)
     w = CONFIGS[args.config or "c3"]
     if w.dtype != "bf16":
         print("the bench times the bf16 entry point; pick a bf16 configuration", file=sys.stderr)
@@ -442,7 +442,8 @@ def bench_backward(args) -> int:
     """fa_bwd on resident inputs (the forward's O and LSE computed once
     beforehand); one JSON line.  Nominal FLOPs: five N^2 d products per head
     (S, dP, dV, dQ, dK), i.e. 2.5 times the forward's, halved for causal; the
-    kernels recompute S and dP (8 products), which is not credited."""
+    kernels recompute S and dP (8 products), which is not credited.  With
+    --dropout P: fa_fwd_dropout, then fa_bwd_dropout with its state."""
     import numpy as np
     import torch
 
@@ -457,7 +458,11 @@ def bench_backward(args) -> int:
     q, k, v = make_inputs(w)
     do = make_grad(w)
     qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, do))
-    o, lse = fa.fwd(qd, kd, vd, causal=w.causal, scale=w.scale)
+    pdrop, seed, offset = float(args.dropout), 0x5EED5EED12345678, 1
+    if pdrop:
+        o, lse, _ = fa.fwd_dropout(qd, kd, vd, pdrop, seed, offset, causal=w.causal, scale=w.scale)
+    else:
+        o, lse = fa.fwd(qd, kd, vd, causal=w.causal, scale=w.scale)
     dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
     need = fa.fa_bwd_workspace_size(w.B, w.Hq, w.N)
     ws = torch.empty(need, dtype=torch.uint8, device=dev)
@@ -465,8 +470,12 @@ def bench_backward(args) -> int:
     ptrs = tuple(t.data_ptr() for t in (qd, kd, vd, o, lse, dod, dq, dk, dv))
 
     def launch():
-        rc = fa.fa_bwd(*ptrs, w.B, w.Hq, w.Hkv, w.N, w.d, int(w.causal), w.scale, ws.data_ptr(),
-                       need, stream.cuda_stream)
+        if pdrop:
+            rc = fa.fa_bwd_dropout(*ptrs, w.B, w.Hq, w.Hkv, w.N, w.d, int(w.causal), w.scale, pdrop, seed,
+                                   offset, ws.data_ptr(), need, stream.cuda_stream)
+        else:
+            rc = fa.fa_bwd(*ptrs, w.B, w.Hq, w.Hkv, w.N, w.d, int(w.causal), w.scale, ws.data_ptr(),
+                           need, stream.cuda_stream)
         if rc != fa.FA_OK:
             raise fa.FaError(rc)
 
@@ -482,8 +491,11 @@ def bench_backward(args) -> int:
         s = np.where(np.arange(w.N)[None, :] > rows[:, None], -np.inf, s)
     p = np.exp(s - s.max(axis=1, keepdims=True))
     p /= p.sum(axis=1, keepdims=True)
-    o_rows = p @ v64[b, hk]
-    dp = do64[b, h, rows] @ v64[b, hk].T
+    # dropout: the oracle's keep bits of these rows, times 1/(1-p)
+    zf = (oracle.dropout_keep(seed, offset, b * w.Hq + h, rows, w.N, pdrop) / (1.0 - float(np.float32(pdrop)))
+          if pdrop else 1.0)
+    o_rows = (p * zf) @ v64[b, hk]
+    dp = (do64[b, h, rows] @ v64[b, hk].T) * zf
     ds = p * (dp - np.sum(do64[b, h, rows] * o_rows, axis=1)[:, None])
     dq_ref = w.scale * (ds @ k64[b, hk])
     err = np.abs(as_f64_numpy(dq)[b, h, rows] - dq_ref)
@@ -491,13 +503,14 @@ def bench_backward(args) -> int:
     ok = bool(err.max() <= 2e-2 * mag)
     flops = 2.5 * w.nominal_flops()
     out = {
-        "metric": "attention bwd TFLOP/s (bf16, nominal 2.5x forward FLOPs)",
+        "metric": "attention bwd TFLOP/s (bf16, nominal 2.5x forward FLOPs)"
+                  + (f", dropout p={pdrop}" if pdrop else ""),
         "value": round(flops * args.steps / (total_ms * 1e-3) / 1e12, 2),
         "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(total_ms / args.steps, 5), "higher_is_better": True,
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": f"{w.name}: {w.note}", "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv,
-                   "N": w.N, "d": w.d, "causal": w.causal, "seed": w.seed,
+                   "N": w.N, "d": w.d, "causal": w.causal, "seed": w.seed, "p_drop": pdrop,
                    "flops_per_step": flops},
         "avg_launch_us": round(avg_ms * 1e3, 2),
         "pct_of_peak": round(100 * flops / (avg_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),

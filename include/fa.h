@@ -209,6 +209,28 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
            void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * fa_bwd_dropout - gradients of an fa_fwd_dropout call.
+ *
+ * With W = P (.) Z / (1 - p_drop) the forward's output was O = W V, so
+ *   dV = W^T dO,  dP = (dO V^T) (.) Z / (1 - p_drop),
+ *   dS = P (.) (dP - D 1^T) with D_i = sum_d dO_id O_id,
+ *   dQ = scale * dS K,  dK = scale * dS^T Q,
+ * the backward of fa_bwd with the dropout factor in the chain rule; Z is
+ * regenerated from (seed, offset), the generator state the reading-notes
+ * page (section 其他算子) has the forward keep for the backward pass.
+ *
+ * Arguments: as for fa_bwd, with o and lse the outputs of the fa_fwd_dropout
+ * call and p_drop, seed, offset exactly the values passed to it.
+ * p_drop = 0 gives fa_bwd's result.  Returns FA_OK or a negative fa_status
+ * (FA_ERR_ARG for p_drop outside [0, 1), otherwise as fa_bwd).
+ */
+int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                   const void* dout, void* dq, void* dk, void* dv,
+                   int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                   float p_drop, unsigned long long seed, unsigned int offset,
+                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * fa_status_string - a static, human-readable description of a status code
  * returned by the entry points above ("unknown status" for anything else).
  * The string is owned by the library and must not be freed.

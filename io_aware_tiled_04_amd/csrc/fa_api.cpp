@@ -140,18 +140,26 @@ extern "C" size_t fa_bwd_workspace_size(int B, int Hq, int N) {
     return (size_t)B * Hq * N * 4;
 }
 
-extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
-                      const void* dout, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int N,
-                      int d, int causal, float scale, void* workspace, size_t workspace_bytes,
-                      hipStream_t stream) {
+namespace {
+
+// Validation and packing shared by the backward entry points.
+int check_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+              void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int N, int d, float scale,
+              const void* workspace, size_t workspace_bytes) {
     if (!dout || !dq || !dk || !dv) return FA_ERR_NULL;
-    int rc = validate(q, k, v, o, lse, B, Hq, Hkv, N, d, scale);
+    const int rc = validate(q, k, v, o, lse, B, Hq, Hkv, N, d, scale);
     if (rc != FA_OK) return rc;
     const long long bh = (long long)B * Hq;
     const long long rtiles = ((long long)N + fa::kBwdBlockRows - 1) / fa::kBwdBlockRows;
     if (bh * rtiles > INT_MAX) return FA_ERR_SHAPE;
     if (!workspace) return FA_ERR_WORKSPACE;
     if ((unsigned long long)B * Hq * N * 4 > (unsigned long long)workspace_bytes) return FA_ERR_WORKSPACE;
+    return FA_OK;
+}
+
+fa::BwdArgs pack_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                     const void* dout, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int N, int d,
+                     int causal, float scale) {
     fa::BwdArgs a;
     a.q = q;
     a.k = k;
@@ -169,7 +177,38 @@ extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o
     a.d = d;
     a.causal = causal != 0;
     a.scale = scale;
-    const hipError_t e = fa::launch_bwd_bf16(a, (float*)workspace, stream);
+    return a;
+}
+
+}  // namespace
+
+extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                      const void* dout, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int N,
+                      int d, int causal, float scale, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
+    const int rc = check_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, N, d, scale, workspace,
+                             workspace_bytes);
+    if (rc != FA_OK) return rc;
+    const hipError_t e = fa::launch_bwd_bf16(pack_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, N, d,
+                                                      causal, scale),
+                                             (float*)workspace, stream);
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+extern "C" int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                              const void* dout, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int N,
+                              int d, int causal, float scale, float p_drop, unsigned long long seed,
+                              unsigned int offset, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream) {
+    int rc = check_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, N, d, scale, workspace, workspace_bytes);
+    if (rc != FA_OK) return rc;
+    fa::Dropout dr;
+    rc = make_dropout(p_drop, seed, offset, &dr);
+    if (rc != FA_OK) return rc;
+    const fa::BwdArgs a = pack_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, N, d, causal, scale);
+    // p = 0: every weight kept with factor 1, the plain backward.
+    const hipError_t e = p_drop == 0.f ? fa::launch_bwd_bf16(a, (float*)workspace, stream)
+                                       : fa::launch_bwd_bf16_dropout(a, dr, (float*)workspace, stream);
     return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

@@ -30,9 +30,21 @@
 //
 // Each workgroup: 4 waves of 32 resident rows (128 rows); streamed tiles of
 // 32 rows, double-buffered in LDS, loaded into registers one tile ahead.
+//
+// Dropout (DROP): the forward's output was O = (P (.) Z) V / (1 - p), so with
+// f = 1 / (1 - p),  dV = (P (.) Z)^T dO f,  dP = (dO V^T) (.) Z f, and
+// dS = P (.) (dP - D) as before (D = rowsum(dO (.) O) with the dropped O
+// still equals sum_j P dP).  The keep bits Z are the forward's (philox.h).
+// DQ holds one query per lane and keys in its registers, the forward's
+// layout: two generator calls per step give its 16 decisions.  DK and DV
+// hold one key per lane: each lane makes the two calls of one streamed query
+// and one half of the wave's keys, and sixteen wave ballots carry the bits
+// to the lanes of their keys.
 #include "fa_kernels.h"
 
 #include <stdint.h>
+
+#include "philox.h"
 
 namespace fa {
 namespace {
@@ -56,6 +68,11 @@ enum Mode { kDQ = 0, kDK = 1, kDV = 2 };
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Keep decision of the draw in 16-bit half `hi` of a generator word.
+__device__ __forceinline__ bool keep_half(uint32_t word, int hi, uint32_t t) {
+    return (hi ? word >> 16 : word & 0xFFFFu) >= t;
 }
 
 // Permuted position of row k (0..31) of a streamed tile inside a transposed
@@ -164,11 +181,13 @@ __global__ __launch_bounds__(256) void bwd_rowdot_kernel(const __bf16* __restric
 //   streamed rows: keys of K/V head (DQ) or queries of the query heads of the
 //   GQA group (DK, DV).
 // c = scale * log2(e) (signed).  LSE and D are [B, Hq, N] float32.
-template <int D, bool CAUSAL, int MODE>
+// DROP: the forward ran with dropout `dr` (see the file header).
+template <int D, bool CAUSAL, int MODE, bool DROP>
 __global__ __launch_bounds__(kThreads, 2) void bwd_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const __bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dd,
-    __bf16* __restrict__ G, int Hq, int Hkv, int N, int n_rtiles, int bh_total, float c, float scale) {
+    __bf16* __restrict__ G, int Hq, int Hkv, int N, int n_rtiles, int bh_total, float c, float scale,
+    Dropout dr) {
     using L = Lay<D>;
     constexpr int KS = D / 16;
     constexpr int DB = D / 32;
@@ -325,6 +344,69 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kernel(
         if (!RES_Q) masked = masked || wr0 + 32 > N;
 
         if (active) {
+            // Dropout keep bits of this wave's pairs (the key j of a pair is
+            // 16a + 8b + 4cc + w; its draw is half 4b + w of the call at
+            // counter (2a + cc, query, query head unit, offset)).
+            //   DQ: lane = query my_row, register i = key row0 + 16(i/8) +
+            //       8((i/4)%2) + 4h + i%4: call i/8 at counter 2(row0/16 + i/8) + h
+            //       holds register i's draw in half i%8.
+            //   DK, DV: zword bit r = keep bit of (query row0 + 4h + r, my key).
+            uint32_t kw[2][4];
+            uint32_t zword = 0;
+            if constexpr (DROP) {
+                const uint32_t t = dr.t2 & 0xFFFFu;
+                // The empty asm hides which counter and key words stay fixed
+                // over the steps; otherwise the optimiser keeps partial rounds
+                // and the ten round keys live across the loop (and spills them).
+                uint32_t k0 = dr.k0, k1 = dr.k1;
+                asm volatile("" : "+s"(k0), "+s"(k1));
+                if constexpr (RES_Q) {
+                    uint32_t row_u = (uint32_t)my_row;
+                    asm volatile("" : "+v"(row_u));
+#pragma unroll
+                    for (int a2 = 0; a2 < 2; ++a2) {
+                        const PhiloxOut r = philox4x32_10((uint32_t)(2 * ((row0 >> 4) + a2) + h), row_u,
+                                                          (uint32_t)bh, dr.offset, k0, k1);
+#pragma unroll
+                        for (int m = 0; m < 4; ++m) kw[a2][m] = r.w[m];
+                    }
+                } else {
+                    // Lane (l32, h) draws for query row0 + l32 and the keys
+                    // wr0 + 16al + 4h + {0..3, 8..11}: bit 8al + k of `mine`
+                    // is half k of call al.
+                    const uint32_t bhq = (uint32_t)(b * Hq + hr * group + step / per_head);
+                    uint32_t mine = 0;
+                    uint32_t ctr0 = (uint32_t)(2 * (wr0 >> 4) + h);
+                    asm volatile("" : "+v"(ctr0));
+#pragma unroll
+                    for (int al = 0; al < 2; ++al) {
+                        const PhiloxOut r = philox4x32_10(ctr0 + 2 * al,
+                                                          (uint32_t)(row0 + l32), bhq, dr.offset, k0, k1);
+#pragma unroll
+                        for (int k = 0; k < 8; ++k)
+                            mine |= (uint32_t)keep_half(r.w[k >> 1], k & 1, t) << (8 * al + k);
+                    }
+                    // My key wr0 + l32 is bit pos of the lanes whose h equals
+                    // its bit 2: lane l32' + 32 * that bit holds query l32'.
+                    // The selection is arithmetic (one-hot `sel`, shift `sh`),
+                    // and the asm keeps the optimiser from hoisting sixteen
+                    // loop-invariant masks out of the step loop.
+                    const int pos = ((l32 >> 4) << 3) | (((l32 >> 3) & 1) << 2) | (l32 & 3);
+                    uint32_t sel = 1u << pos;
+                    uint32_t sh = ((l32 >> 2) & 1) * 32u;
+                    asm volatile("" : "+v"(sel), "+v"(sh));
+#pragma unroll
+                    for (int bit = 0; bit < 16; ++bit) {
+                        const uint64_t bal = __builtin_amdgcn_ballot_w64((mine >> bit) & 1u);
+                        zword |= (uint32_t)(bal >> sh) & (0u - ((sel >> bit) & 1u));
+                    }
+                    // Register i's query is (i/4)*8 + 4h + i%4: shift out 4h
+                    // here so that the per-element shifts are immediates (a
+                    // per-lane shift count per element would be 16 registers
+                    // kept across the loop).
+                    zword >>= 4 * h;
+                }
+            }
             // score products: X = A_tile (rows) x resident^T, one resident row per lane
             const LDS char* arow = base + L::A + l32 * L::RPITCH + 16 * h;
             f32x16 x = (f32x16){};
@@ -370,8 +452,14 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kernel(
                 bool dead = false;
                 if (masked) dead = key >= N || qry >= N || (CAUSAL && key > qry);
                 const float p = dead ? 0.f : __builtin_amdgcn_exp2f(fmaf(x[i], c, -lse2));
+                bool kept = true;
+                if constexpr (DROP) {
+                    if constexpr (RES_Q) kept = keep_half(kw[i >> 3][(i & 7) >> 1], i & 1, dr.t2 & 0xFFFFu);
+                    else kept = (zword >> ((i >> 2) * 8 + (i & 3))) & 1u;
+                }
                 float val;
-                if constexpr (MODE == kDV) val = p;
+                if constexpr (MODE == kDV) val = kept ? p : 0.f;              // times f in the epilogue
+                else if constexpr (DROP) val = p * ((kept ? y[i] * dr.factor : 0.f) - dv);
                 else val = p * (y[i] - dv);
                 w[i >> 3][i & 7] = (__bf16)val;
             }
@@ -391,7 +479,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kernel(
 
     // Epilogue: this lane's resident row, d = 32*db + 8*g + 4*h + r.
     if (my_row >= N) return;
-    const float f = MODE == kDV ? 1.f : scale;
+    const float f = MODE == kDV ? (DROP ? dr.factor : 1.f) : scale;
     __bf16* gp = G + rhead + (size_t)my_row * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -404,8 +492,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kernel(
         }
 }
 
-template <int D, bool CAUSAL, int MODE>
-hipError_t launch_mode(const BwdArgs& a, const float* dd, hipStream_t stream) {
+template <int D, bool CAUSAL, int MODE, bool DROP>
+hipError_t launch_mode(const BwdArgs& a, const float* dd, const Dropout& drop, hipStream_t stream) {
     int n_rtiles = (a.N + kRows - 1) / kRows;
     int bh_total = a.B * (MODE == kDQ ? a.Hq : a.Hkv);
     float c = a.scale * kLog2e;
@@ -417,14 +505,15 @@ hipError_t launch_mode(const BwdArgs& a, const float* dd, hipStream_t stream) {
     const __bf16* dO = (const __bf16*)a.dO;
     const float* lse = a.lse;
     __bf16* g = (__bf16*)(MODE == kDQ ? a.dq : MODE == kDK ? a.dk : a.dv);
+    Dropout dr = drop;
     void* args[] = {(void*)&q, (void*)&k, (void*)&v, (void*)&dO, (void*)&lse, (void*)&dd, &g,
-                    &Hq, &Hkv, &N, &n_rtiles, &bh_total, &c, &scale};
-    return hipLaunchKernel((const void*)bwd_kernel<D, CAUSAL, MODE>, dim3(bh_total * n_rtiles),
+                    &Hq, &Hkv, &N, &n_rtiles, &bh_total, &c, &scale, &dr};
+    return hipLaunchKernel((const void*)bwd_kernel<D, CAUSAL, MODE, DROP>, dim3(bh_total * n_rtiles),
                            dim3(kThreads), args, 0, stream);
 }
 
-template <int D, bool CAUSAL>
-hipError_t launch_all(const BwdArgs& a, float* workspace, hipStream_t stream) {
+template <int D, bool CAUSAL, bool DROP>
+hipError_t launch_all(const BwdArgs& a, float* workspace, const Dropout& dr, hipStream_t stream) {
     long long rows = (long long)a.B * a.Hq * a.N;
     const __bf16* dO = (const __bf16*)a.dO;
     const __bf16* o = (const __bf16*)a.o;
@@ -435,17 +524,28 @@ hipError_t launch_all(const BwdArgs& a, float* workspace, hipStream_t stream) {
                                    dim3((unsigned)((rows + per_block - 1) / per_block)), dim3(256), args,
                                    0, stream);
     if (e != hipSuccess) return e;
-    if ((e = launch_mode<D, CAUSAL, kDQ>(a, dd, stream)) != hipSuccess) return e;
-    if ((e = launch_mode<D, CAUSAL, kDK>(a, dd, stream)) != hipSuccess) return e;
-    return launch_mode<D, CAUSAL, kDV>(a, dd, stream);
+    if ((e = launch_mode<D, CAUSAL, kDQ, DROP>(a, dd, dr, stream)) != hipSuccess) return e;
+    if ((e = launch_mode<D, CAUSAL, kDK, DROP>(a, dd, dr, stream)) != hipSuccess) return e;
+    return launch_mode<D, CAUSAL, kDV, DROP>(a, dd, dr, stream);
 }
 
 }  // namespace
 
 hipError_t launch_bwd_bf16(const BwdArgs& a, float* workspace, hipStream_t stream) {
+    const Dropout none{};
     if (a.d == 128)
-        return a.causal ? launch_all<128, true>(a, workspace, stream) : launch_all<128, false>(a, workspace, stream);
-    return a.causal ? launch_all<64, true>(a, workspace, stream) : launch_all<64, false>(a, workspace, stream);
+        return a.causal ? launch_all<128, true, false>(a, workspace, none, stream)
+                        : launch_all<128, false, false>(a, workspace, none, stream);
+    return a.causal ? launch_all<64, true, false>(a, workspace, none, stream)
+                    : launch_all<64, false, false>(a, workspace, none, stream);
+}
+
+hipError_t launch_bwd_bf16_dropout(const BwdArgs& a, const Dropout& dr, float* workspace, hipStream_t stream) {
+    if (a.d == 128)
+        return a.causal ? launch_all<128, true, true>(a, workspace, dr, stream)
+                        : launch_all<128, false, true>(a, workspace, dr, stream);
+    return a.causal ? launch_all<64, true, true>(a, workspace, dr, stream)
+                    : launch_all<64, false, true>(a, workspace, dr, stream);
 }
 
 }  // namespace fa

@@ -57,6 +57,8 @@ hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
 // Backward pass: D = rowsum(dO * O) into `workspace` (B*Hq*N floats), then
 // the dQ, dK and dV kernels, all enqueued on `stream`.
 hipError_t launch_bwd_bf16(const BwdArgs& a, float* workspace, hipStream_t stream);
+// launch_bwd_bf16 for a forward that ran with dropout `dr`.
+hipError_t launch_bwd_bf16_dropout(const BwdArgs& a, const Dropout& dr, float* workspace, hipStream_t stream);
 
 // Query rows per workgroup of the bf16 kernel (the grid is B*Hq*ceil(N/kBlockRowsBf16)).
 constexpr int kBlockRowsBf16 = 256;

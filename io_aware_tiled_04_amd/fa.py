@@ -30,7 +30,7 @@ FA_ERR_WORKSPACE = -7
 
 # Names declared in include/fa.h, in order.
 EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_fwd_splitkv_workspace_size", "fa_fwd_splitkv",
-           "fa_fwd_dropout", "fa_bwd_workspace_size", "fa_bwd", "fa_status_string")
+           "fa_fwd_dropout", "fa_bwd_workspace_size", "fa_bwd", "fa_bwd_dropout", "fa_status_string")
 
 
 def _load():
@@ -55,6 +55,10 @@ def _load():
     lib.fa_bwd.argtypes = [ctypes.c_void_p] * 9 + [ctypes.c_int] * 6 + \
         [ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     lib.fa_bwd.restype = ctypes.c_int
+    lib.fa_bwd_dropout.argtypes = [ctypes.c_void_p] * 9 + [ctypes.c_int] * 6 + \
+        [ctypes.c_float, ctypes.c_float, ctypes.c_ulonglong, ctypes.c_uint, ctypes.c_void_p, ctypes.c_size_t,
+         ctypes.c_void_p]
+    lib.fa_bwd_dropout.restype = ctypes.c_int
     lib.fa_bwd_workspace_size.argtypes = [ctypes.c_int] * 3
     lib.fa_bwd_workspace_size.restype = ctypes.c_size_t
     lib.fa_status_string.argtypes = [ctypes.c_int]
@@ -115,6 +119,14 @@ def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, N, d, causal, scale, w
     """Raw call of the backward C entry point; pointers and stream are integers."""
     return _lib.fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, N, d, int(causal),
                        float(scale), workspace, int(workspace_bytes), stream)
+
+
+def fa_bwd_dropout(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, N, d, causal, scale, p_drop, seed,
+                   offset, workspace, workspace_bytes, stream) -> int:
+    """Raw call of the dropout backward C entry point; pointers and stream are integers."""
+    return _lib.fa_bwd_dropout(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, N, d, int(causal),
+                               float(scale), float(p_drop), int(seed) & 0xFFFFFFFFFFFFFFFF,
+                               int(offset) & 0xFFFFFFFF, workspace, int(workspace_bytes), stream)
 
 
 def _check(t, name, dtype, device):
@@ -232,11 +244,12 @@ def fwd_dropout(q, k, v, p_drop: float, seed: int, offset: int = 0, causal: bool
 
 
 def bwd(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None, workspace=None,
-        stream=None):
+        stream=None, dropout=None):
     """Gradients (dQ, dK, dV) of a bf16 forward pass from its saved o and lse
     and the upstream gradient ``dout``; allocates the outputs (and the
     workspace when it is None) on q's device and launches on ``stream`` or
-    torch's current stream."""
+    torch's current stream.  ``dropout`` = (p_drop, (seed, offset)) for a
+    forward run by ``fwd_dropout`` (its o, lse and returned state)."""
     import torch
     dev = q.device
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
@@ -258,9 +271,15 @@ def bwd(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None,
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)
     s = (stream if stream is not None else torch.cuda.current_stream(dev)).cuda_stream
-    rc = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Hq, Hkv, N, d,
-                causal, scale, workspace.data_ptr(), workspace.numel() * workspace.element_size(), s)
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+            dq.data_ptr(), dk.data_ptr(), dv.data_ptr())
+    wsz = workspace.numel() * workspace.element_size()
+    if dropout is None:
+        rc = fa_bwd(*ptrs, B, Hq, Hkv, N, d, causal, scale, workspace.data_ptr(), wsz, s)
+    else:
+        p_drop, (seed, offset) = dropout
+        rc = fa_bwd_dropout(*ptrs, B, Hq, Hkv, N, d, causal, scale, p_drop, seed, offset,
+                            workspace.data_ptr(), wsz, s)
     if rc != FA_OK:
         raise FaError(rc)
     return dq, dk, dv

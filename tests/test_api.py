@@ -22,7 +22,7 @@ def _declared():
 def test_header_declares_the_entry_points():
     assert _declared() == ["fa_fwd", "fa_fwd_f32", "fa_fwd_splitkv_workspace_size",
                            "fa_fwd_splitkv", "fa_fwd_dropout", "fa_bwd_workspace_size", "fa_bwd",
-                           "fa_status_string"]
+                           "fa_bwd_dropout", "fa_status_string"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -154,6 +154,28 @@ def test_backward_rejects_invalid_arguments(ptrs, sizes, ws, expect):
     from io_aware_tiled_04_amd import fa
     rc = fa.fa_bwd(*ptrs, *sizes, *ws, 0)
     assert rc == getattr(fa, expect), (rc, fa.fa_status_string(rc))
+
+
+def test_backward_dropout_rejects_invalid_arguments():
+    """fa_bwd_dropout runs fa_bwd's checks, then checks p_drop."""
+    from io_aware_tiled_04_amd import fa
+    ptrs = (P,) * 9
+    sizes = (1, 2, 1, 128, 64, 1, 0.125)
+    ws = (P, 1 << 20)
+    cases = [
+        ((0,) + ptrs[1:], sizes, 0.1, ws, "FA_ERR_NULL"),
+        (ptrs[:5] + (0,) + ptrs[6:], sizes, 0.1, ws, "FA_ERR_NULL"),
+        (ptrs, (1, 3, 2, 128, 64, 1, 0.125), 0.1, ws, "FA_ERR_HEADS"),
+        (ptrs, (1, 2, 1, 128, 96, 1, 0.125), 0.1, ws, "FA_ERR_HEADDIM"),
+        (ptrs, sizes, 0.1, (0, 1 << 20), "FA_ERR_WORKSPACE"),
+        (ptrs, sizes, 0.1, (P, 2 * 128 * 4 - 1), "FA_ERR_WORKSPACE"),
+        (ptrs, sizes, -0.5, ws, "FA_ERR_ARG"),
+        (ptrs, sizes, 1.0, ws, "FA_ERR_ARG"),
+        (ptrs, sizes, math.nan, ws, "FA_ERR_ARG"),
+    ]
+    for p_, sz, pd, w_, expect in cases:
+        rc = fa.fa_bwd_dropout(*p_, *sz, pd, 3, 1, *w_, 0)
+        assert rc == getattr(fa, expect), (p_, sz, pd, w_, rc, fa.fa_status_string(rc))
 
 
 def test_backward_workspace_size():
