@@ -144,6 +144,8 @@ def main() -> int:
     ap.add_argument("--splitkv", type=int, default=0,
                     help="time fa_fwd_splitkv with this many splits (and fa_fwd beside it)")
     ap.add_argument("--backward", action="store_true", help="time the backward pass (fa_bwd)")
+    ap.add_argument("--kvouter", action="store_true",
+                    help="time fa_fwd_kvouter (the K/V-outer loop order) beside fa_fwd")
     ap.add_argument("--dropout", type=float, default=0.0,
                     help="time fa_fwd_dropout with this drop probability (and fa_fwd beside it)")
     args = ap.parse_args()
@@ -168,6 +170,8 @@ def main() -> int:
         return bench_splitkv(args)
     if args.backward:
         return bench_backward(args)
+    if args.kvouter:
+        return bench_kvouter(args)
     if args.dropout:
         return bench_dropout(args)
     w = CONFIGS[args.config or "c3"]
@@ -212,11 +216,7 @@ def main() -> int:
     avg_launch_ms = sum(launch_ms) / len(launch_ms)
 
     if args.calibrate_copy:
-        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            torch.mul(src, 1.0, out=dst)
-        torch.cuda.synchronize()
+        _calibrate_copy(dev)
 
     # parity of the timed outputs on sampled rows (oracle row by row)
     rng = np.random.default_rng(0)
@@ -268,6 +268,17 @@ def main() -> int:
         out["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_seconds)
     print(json.dumps(out), flush=True)
     return 0 if parity_ok else 1
+
+
+def _calibrate_copy(dev):
+    """Three elementwise copies of COPY_BYTES (read and write COPY_BYTES
+    each): the reference that scales FETCH_SIZE / WRITE_SIZE to bytes."""
+    import torch
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
 
 
 def _time_launches(launch, stream, steps, warmup):
@@ -431,6 +442,103 @@ def bench_dropout(args) -> int:
         "dropout_tflops_per_launch": round(flops / (drop_ms * 1e-3) / 1e12, 2),
         "direct_tflops_per_launch": round(flops / (direct_ms * 1e-3) / 1e12, 2),
         "slowdown_vs_direct": round(drop_ms / direct_ms, 3),
+        "parity": {"rows": len(rows), "max_abs_o": float(err.max()), "mean_abs_o": float(err.mean()),
+                   "max_abs_lse": float(lerr.max()), "ok": ok},
+    }
+    print(json.dumps(out), flush=True)
+    return 0 if ok else 1
+
+
+def kvouter_structural_bytes(w) -> dict:
+    """Bytes the K/V-outer loop order moves by construction, from the loop
+    structure of fa_fwd_kvouter: K and V once per head; per visible (32-row
+    query block, 64-key tile) pair the block's Q (bf16), and its fp32 output
+    accumulator plus row max and row sum read (all but the first tile) and
+    written (all but the last); O (bf16) and LSE written once."""
+    d, N, heads = w.d, w.N, w.B * w.Hq
+    nblk, ntile = -(-N // 32), -(-N // 64)
+    pairs = reads = writes = 0
+    for rb in range(nblk):
+        last = min(ntile - 1, (min(N, 32 * rb + 32) - 1) // 64) if w.causal else ntile - 1
+        pairs += last + 1
+        reads += last          # tiles 1..last read the state
+        writes += last         # tiles 0..last-1 write it
+    state = 32 * d * 4 + 2 * 64 * 4      # O accumulator + per-lane m and l of one block
+    per_head = pairs * 32 * d * 2 + (reads + writes) * state
+    kv = w.B * w.Hkv * N * d * 2 * 2
+    out = heads * N * d * 2 + heads * N * 4
+    return {"pairs_per_head": pairs, "read_bytes": heads * (pairs * 32 * d * 2 + reads * state) + kv,
+            "write_bytes": heads * writes * state + out,
+            "total_bytes": heads * per_head + kv + out}
+
+
+def bench_kvouter(args) -> int:
+    """fa_fwd_kvouter against fa_fwd on the same resident inputs (default c3);
+    one JSON line with both per-launch times and the K/V-outer order's
+    structural bytes.  Parity: sampled rows against the oracle."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from io_aware_tiled_04_amd import fa
+    from io_aware_tiled_04_amd.workloads import CONFIGS, EXTRA, as_f64_numpy, make_inputs
+
+    name = args.config or "c3"
+    w = EXTRA.get(name) or CONFIGS[name]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q, k, v = make_inputs(w)
+    qd, kd, vd = (t.to(dev) for t in (q, k, v))
+    o = torch.empty_like(qd)
+    lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device=dev)
+    need = fa.fa_fwd_kvouter_workspace_size(w.B, w.Hq, w.N, w.d)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    ptrs = (qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(), lse.data_ptr())
+
+    def launch_direct():
+        rc = fa.fa_fwd(*ptrs, w.B, w.Hq, w.Hkv, w.N, w.d, int(w.causal), w.scale, stream.cuda_stream)
+        if rc != fa.FA_OK:
+            raise fa.FaError(rc)
+
+    def launch_kv():
+        rc = fa.fa_fwd_kvouter(*ptrs, w.B, w.Hq, w.Hkv, w.N, w.d, int(w.causal), w.scale, ws.data_ptr(), need,
+                               stream.cuda_stream)
+        if rc != fa.FA_OK:
+            raise fa.FaError(rc)
+
+    direct_ms, _ = _time_launches(launch_direct, stream, args.steps, args.warmup)
+    kv_ms, kv_total = _time_launches(launch_kv, stream, args.steps, args.warmup)
+    if args.calibrate_copy:
+        _calibrate_copy(dev)
+
+    rng = np.random.default_rng(0)
+    rows = [(0, 0, 0), (w.B - 1, w.Hq - 1, w.N - 1)] + [
+        (int(rng.integers(0, w.B)), int(rng.integers(0, w.Hq)), int(rng.integers(0, w.N))) for _ in range(30)]
+    o_ref, lse_ref = oracle.attention_rows(as_f64_numpy(q), as_f64_numpy(k), as_f64_numpy(v), w.causal, w.scale,
+                                           rows)
+    idx = tuple(np.array(rows).T)
+    err = np.abs(as_f64_numpy(o)[idx] - o_ref)
+    lerr = np.abs(as_f64_numpy(lse)[idx] - lse_ref)
+    ok = bool(err.max() <= 2e-2 and err.mean() <= 2e-3 and lerr.max() <= 1e-3)
+    flops = w.nominal_flops()
+    sb = kvouter_structural_bytes(w)
+    alg = w.B * w.Hq * w.N * w.d * 2 * 2 + w.B * w.Hkv * w.N * w.d * 2 * 2 + w.B * w.Hq * w.N * 4
+    out = {
+        "metric": "attention fwd TFLOP/s, K/V-outer loop order (bf16)",
+        "value": round(flops * args.steps / (kv_total * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(kv_total / args.steps, 5), "higher_is_better": True,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{w.name}: {w.note}", "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "d": w.d,
+                   "causal": w.causal, "seed": w.seed, "flops_per_step": flops},
+        "kernel": f"fwd_kvouter_kernel<{w.d}, {'causal' if w.causal else 'full'}>",
+        "kvouter_avg_launch_us": round(kv_ms * 1e3, 2),
+        "direct_avg_launch_us": round(direct_ms * 1e3, 2),
+        "slowdown_vs_direct": round(kv_ms / direct_ms, 3),
+        "algorithmic_bytes": alg,
+        "kvouter_structural_bytes": sb["total_bytes"],
+        "kvouter_structural_GBps": round(sb["total_bytes"] / (kv_ms * 1e-3) / 1e9, 1),
         "parity": {"rows": len(rows), "max_abs_o": float(err.max()), "mean_abs_o": float(err.mean()),
                    "max_abs_lse": float(lerr.max()), "ok": ok},
     }

@@ -167,6 +167,38 @@ int fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* 
                    hipStream_t stream);
 
 /*
+ * fa_fwd_kvouter_workspace_size - bytes of device workspace fa_fwd_kvouter
+ * needs: B * Hq * ceil(N/32) * (32 * d + 128) * 4 (the running output, row
+ * max and row sum of every 32-row query block, float32).  Returns 0 for
+ * arguments fa_fwd_kvouter would reject.
+ */
+size_t fa_fwd_kvouter_workspace_size(int B, int Hq, int N, int d);
+
+/*
+ * fa_fwd_kvouter - the result of fa_fwd (same o and lse up to float rounding
+ * order), computed in the loop order of the reading-notes page (Methods):
+ * the K/V blocks are the outer loop, each read from HBM once per head, and
+ * for every K/V block the query blocks read their Q, running output O and
+ * row statistics m, l from device memory, apply the page's two rescaling
+ * equations and write them back.  fa_fwd keeps the query block on chip
+ * instead (the interchanged order).  This entry point exists to measure that
+ * trade: one workgroup per (batch, head), and HBM traffic that grows with
+ * N^2 / 64 instead of N.
+ *
+ * Arguments q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, stream: as for
+ *   fa_fwd.
+ * workspace: device memory of at least fa_fwd_kvouter_workspace_size(B, Hq,
+ *   N, d) bytes, 16-byte aligned, owned by the caller; its contents on entry
+ *   do not matter; it must not be shared with a call that runs at the same
+ *   time.
+ * Returns FA_OK or a negative fa_status (FA_ERR_WORKSPACE for a null,
+ * misaligned or small workspace, otherwise as fa_fwd).
+ */
+int fa_fwd_kvouter(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * fa_bwd_workspace_size - bytes of device workspace that fa_bwd needs:
  * B * Hq * N * 4 (one float32 per query row).  Returns 0 for non-positive
  * sizes.

@@ -9,7 +9,8 @@ without loading the GPU library.
 
 
 def __getattr__(name):
-    if name in ("fwd", "fwd_splitkv", "fwd_dropout", "bwd", "fa_fwd", "fa_fwd_f32", "fa_fwd_splitkv",
+    if name in ("fwd", "fwd_splitkv", "fwd_dropout", "fwd_kvouter", "bwd", "fa_fwd_kvouter",
+                "fa_fwd_kvouter_workspace_size", "fa_fwd", "fa_fwd_f32", "fa_fwd_splitkv",
                 "fa_fwd_splitkv_workspace_size", "fa_fwd_dropout", "fa_bwd", "fa_bwd_dropout",
                 "fa_bwd_workspace_size",
                 "fa_status_string", "FaError"):

@@ -4,6 +4,7 @@
 #include "fa.h"
 
 #include <climits>
+#include <cstdint>
 #include <cmath>
 
 #include "fa_kernels.h"
@@ -131,6 +132,25 @@ extern "C" int fa_fwd_splitkv(const void* q, const void* k, const void* v, void*
     if (rc != FA_OK) return rc;
     const hipError_t e = fa::launch_fwd_bf16_split(pack(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale),
                                                    num_splits, (float*)workspace, stream);
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+extern "C" size_t fa_fwd_kvouter_workspace_size(int B, int Hq, int N, int d) {
+    if (B <= 0 || Hq <= 0 || N <= 0 || (d != 64 && d != 128)) return 0;
+    if ((double)B * Hq * (double)N * 128.0 >= 1125899906842624.0) return 0;
+    return (size_t)fa::kvouter_workspace_floats(B, Hq, N, d) * 4;
+}
+
+extern "C" int fa_fwd_kvouter(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+                              int Hkv, int N, int d, int causal, float scale, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
+    const int rc = validate(q, k, v, o, lse, B, Hq, Hkv, N, d, scale);
+    if (rc != FA_OK) return rc;
+    if (!workspace || ((uintptr_t)workspace & 15) != 0) return FA_ERR_WORKSPACE;
+    if ((unsigned long long)fa::kvouter_workspace_floats(B, Hq, N, d) * 4 > (unsigned long long)workspace_bytes)
+        return FA_ERR_WORKSPACE;
+    const hipError_t e = fa::launch_fwd_bf16_kvouter(pack(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale),
+                                                     (float*)workspace, stream);
     return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

@@ -54,6 +54,11 @@ hipError_t launch_fwd_bf16_split(const FwdArgs& a, int n_splits, float* workspac
 // weights before dropout).
 hipError_t launch_fwd_bf16_dropout(const FwdArgs& a, const Dropout& dr, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
+// The forward in the K/V-outer loop order: one workgroup per (batch, head),
+// the running O, m and l of each 32-row query block in `workspace` (float32,
+// kvouter_workspace_floats(...) elements).
+hipError_t launch_fwd_bf16_kvouter(const FwdArgs& a, float* workspace, hipStream_t stream);
+long long kvouter_workspace_floats(long long B, long long Hq, long long N, long long d);
 // Backward pass: D = rowsum(dO * O) into `workspace` (B*Hq*N floats), then
 // the dQ, dK and dV kernels, all enqueued on `stream`.
 hipError_t launch_bwd_bf16(const BwdArgs& a, float* workspace, hipStream_t stream);

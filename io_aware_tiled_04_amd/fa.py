@@ -30,7 +30,8 @@ FA_ERR_WORKSPACE = -7
 
 # Names declared in include/fa.h, in order.
 EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_fwd_splitkv_workspace_size", "fa_fwd_splitkv",
-           "fa_fwd_dropout", "fa_bwd_workspace_size", "fa_bwd", "fa_bwd_dropout", "fa_status_string")
+           "fa_fwd_dropout", "fa_fwd_kvouter_workspace_size", "fa_fwd_kvouter", "fa_bwd_workspace_size",
+           "fa_bwd", "fa_bwd_dropout", "fa_status_string")
 
 
 def _load():
@@ -50,6 +51,10 @@ def _load():
     lib.fa_fwd_dropout.argtypes = fwd_args[:-1] + [ctypes.c_float, ctypes.c_ulonglong, ctypes.c_uint,
                                                    ctypes.c_void_p]
     lib.fa_fwd_dropout.restype = ctypes.c_int
+    lib.fa_fwd_kvouter.argtypes = fwd_args[:-1] + [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.fa_fwd_kvouter.restype = ctypes.c_int
+    lib.fa_fwd_kvouter_workspace_size.argtypes = [ctypes.c_int] * 4
+    lib.fa_fwd_kvouter_workspace_size.restype = ctypes.c_size_t
     lib.fa_fwd_splitkv_workspace_size.argtypes = [ctypes.c_int] * 5
     lib.fa_fwd_splitkv_workspace_size.restype = ctypes.c_size_t
     lib.fa_bwd.argtypes = [ctypes.c_void_p] * 9 + [ctypes.c_int] * 6 + \
@@ -107,6 +112,18 @@ def fa_fwd_dropout(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, p_drop, see
     return _lib.fa_fwd_dropout(q, k, v, o, lse, B, Hq, Hkv, N, d, int(causal), float(scale),
                                float(p_drop), int(seed) & 0xFFFFFFFFFFFFFFFF,
                                int(offset) & 0xFFFFFFFF, stream)
+
+
+def fa_fwd_kvouter_workspace_size(B, Hq, N, d) -> int:
+    """Bytes of workspace the K/V-outer entry point needs (0 for invalid sizes)."""
+    return int(_lib.fa_fwd_kvouter_workspace_size(B, Hq, N, d))
+
+
+def fa_fwd_kvouter(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, workspace, workspace_bytes,
+                   stream) -> int:
+    """Raw call of the K/V-outer C entry point; pointers and stream are integers."""
+    return _lib.fa_fwd_kvouter(q, k, v, o, lse, B, Hq, Hkv, N, d, int(causal), float(scale), workspace,
+                               int(workspace_bytes), stream)
 
 
 def fa_bwd_workspace_size(B, Hq, N) -> int:
@@ -241,6 +258,36 @@ def fwd_dropout(q, k, v, p_drop: float, seed: int, offset: int = 0, causal: bool
     if rc != FA_OK:
         raise FaError(rc)
     return o, lse, (int(seed) & 0xFFFFFFFFFFFFFFFF, int(offset) & 0xFFFFFFFF)
+
+
+def fwd_kvouter(q, k, v, causal: bool = False, scale: float | None = None, workspace=None, stream=None):
+    """The forward in the K/V-outer loop order on bf16 tensors: returns
+    (O, LSE), fa_fwd's result up to float rounding order.  ``workspace``: an
+    optional uint8 device tensor of at least fa_fwd_kvouter_workspace_size
+    bytes (allocated when None)."""
+    import torch
+    dev = q.device
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, n, torch.bfloat16, dev)
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    if tuple(k.shape) != (B, Hkv, N, d) or tuple(v.shape) != (B, Hkv, N, d):
+        raise ValueError("k and v must be [B, Hkv, N, d] with q's B, N and d")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = fa_fwd_kvouter_workspace_size(B, Hq, N, d)
+    if need == 0:
+        raise ValueError("invalid sizes for the K/V-outer forward")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
+    s = (stream if stream is not None else torch.cuda.current_stream(dev)).cuda_stream
+    rc = fa_fwd_kvouter(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, Hq, Hkv, N, d,
+                        causal, scale, workspace.data_ptr(), workspace.numel() * workspace.element_size(), s)
+    if rc != FA_OK:
+        raise FaError(rc)
+    return o, lse
 
 
 def bwd(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None, workspace=None,

@@ -21,8 +21,9 @@ def _declared():
 
 def test_header_declares_the_entry_points():
     assert _declared() == ["fa_fwd", "fa_fwd_f32", "fa_fwd_splitkv_workspace_size",
-                           "fa_fwd_splitkv", "fa_fwd_dropout", "fa_bwd_workspace_size", "fa_bwd",
-                           "fa_bwd_dropout", "fa_status_string"]
+                           "fa_fwd_splitkv", "fa_fwd_dropout", "fa_fwd_kvouter_workspace_size",
+                           "fa_fwd_kvouter", "fa_bwd_workspace_size", "fa_bwd", "fa_bwd_dropout",
+                           "fa_status_string"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -135,6 +136,28 @@ def test_dropout_rejects_invalid_arguments():
     for args, p, expect in cases:
         rc = fa.fa_fwd_dropout(*args, p, 7, 0, 0)
         assert rc == getattr(fa, expect), (args, p, rc, fa.fa_status_string(rc))
+
+
+def test_kvouter_validation_and_workspace_size():
+    from io_aware_tiled_04_amd import fa
+    assert fa.fa_fwd_kvouter_workspace_size(2, 32, 4096, 128) == 2 * 32 * 128 * (32 * 128 + 128) * 4
+    assert fa.fa_fwd_kvouter_workspace_size(1, 1, 33, 64) == 2 * (32 * 64 + 128) * 4
+    for bad in [(0, 1, 64, 64), (1, 0, 64, 64), (1, 1, 0, 64), (1, 1, 64, 96)]:
+        assert fa.fa_fwd_kvouter_workspace_size(*bad) == 0, bad
+    need = fa.fa_fwd_kvouter_workspace_size(1, 2, 300, 64)
+    base = (P, P, P, P, P, 1, 2, 1, 300, 64, 1, 0.125)
+    cases = [
+        ((0,) + base[1:], (P, need), "FA_ERR_NULL"),
+        (base[:5] + (1, 3, 2) + base[8:], (P, need), "FA_ERR_HEADS"),
+        (base[:9] + (80,) + base[10:], (P, need), "FA_ERR_HEADDIM"),
+        (base[:11] + (math.inf,), (P, need), "FA_ERR_ARG"),
+        (base, (0, need), "FA_ERR_WORKSPACE"),
+        (base, (P + 4, need), "FA_ERR_WORKSPACE"),       # not 16-byte aligned
+        (base, (P, need - 1), "FA_ERR_WORKSPACE"),
+    ]
+    for args, (ws, wbytes), expect in cases:
+        rc = fa.fa_fwd_kvouter(*args, ws, wbytes, 0)
+        assert rc == getattr(fa, expect), (args, ws, wbytes, rc, fa.fa_status_string(rc))
 
 
 @pytest.mark.parametrize("ptrs,sizes,ws,expect", [
