@@ -400,14 +400,21 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     // Work decomposition.  Workgroups are dealt round-robin to the 8 XCDs
     // (w % 8); give each XCD a contiguous range of heads so that the query
     // tiles sharing one K/V head (and a GQA group) share that XCD's L2 and
-    // MALL slice.  Within an XCD, query tiles go out in rounds over its heads,
-    // latest (heaviest, when causal) tiles first, so the short tiles fill the
-    // tail of the launch.
+    // MALL slice.  Within an XCD the heads go four at a time, and the query
+    // tiles of those four go out in rounds over them, latest (heaviest, when
+    // causal) tiles first: four heads keep the K/V being read within the
+    // XCD's L2 (half the L2 misses of rounds over all its heads, at the same
+    // speed), and the short tiles of each group fill in behind the long ones.
     int bh, qt;
     const int split = SPLIT ? (int)blockIdx.y : 0;
     {
         const int w = blockIdx.x;
-        if ((bh_total & 7) == 0) {
+        if ((bh_total & 31) == 0) {
+            const int slot = w >> 3;
+            const int r = slot % (4 * n_qtiles);
+            bh = (w & 7) * (bh_total >> 3) + 4 * (slot / (4 * n_qtiles)) + (r & 3);
+            qt = r >> 2;
+        } else if ((bh_total & 7) == 0) {
             const int slot = w >> 3;
             bh = (w & 7) * (bh_total >> 3) + slot % (bh_total >> 3);
             qt = slot / (bh_total >> 3);

@@ -73,6 +73,9 @@ SMALL = [
     Workload("f32-d128-causal", 1, 2, 1, 150, 128, True, "f32", 69),
     Workload("f32-d64-ragged", 2, 1, 1, 77, 64, False, "f32", 70),
     Workload("f32-N1", 1, 1, 1, 1, 64, True, "f32", 71),
+    # 32 and 64 query heads: the XCD work order that takes heads four at a time
+    Workload("h32-gqa-ragged", 1, 32, 8, 300, 64, True, "bf16", 72),
+    Workload("h64-noncausal-ragged", 2, 32, 32, 130, 128, False, "bf16", 73),
 ]
 
 
