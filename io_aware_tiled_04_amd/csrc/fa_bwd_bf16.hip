@@ -14,32 +14,31 @@
 // (the section's dV, dP, dQ and dK equations, with the softmax scale of the
 // forward; D is the diag(dO O^T) term of the blog's standard backward).
 //
-// Kernels.  The accumulators of one 32-row block at d = 128 take 64 VGPRs
-// each, so one wave cannot hold dK and dV (and K, V, S and dP) within the 256
-// VGPRs of two waves per SIMD.  The work is split in three kernels of the
-// forward's size, each with one accumulator:
-//   DQ: resident query rows, streamed key tiles:  S^T = K Q^T and
-//       dP^T = V dO^T put one query per lane (LSE and D per lane), and
-//       dQ^T += K^T dS^T takes K^T from LDS in the key order of dS^T's
-//       registers (the forward's V^T trick).
-//   DK: resident key rows, streamed query tiles: S = Q K^T and dP = dO V^T
-//       put one key per lane, and dK^T += Q^T dS takes Q^T from LDS.
-//   DV: resident key rows: S = Q K^T, then dV^T += dO^T P.
-// S and dP are recomputed by the kernels that need them (8 products instead
-// of 5).  A first kernel forms D.
-//
-// Each workgroup: 4 waves of 32 resident rows (128 rows); streamed tiles of
-// 32 rows, double-buffered in LDS, loaded into registers one tile ahead.
+// Kernels.
+//   D:   rowdot kernel, D_i = sum_d dO_id O_id.
+//   dQ:  resident query rows, streamed key tiles: S^T = K Q^T and
+//        dP^T = V dO^T put one query per lane (LSE and D per lane), and
+//        dQ^T += K^T dS^T takes K^T from LDS in the key order of dS^T's
+//        registers (the forward's V^T trick).  4 waves of 32 rows.
+//   dK, dV: one launch (bwd_dkv_kernel below): resident key rows, streamed
+//        query tiles, 8 waves in pairs: one wave of a pair forms S, P and
+//        then dS and dK, the other dP and then dV, exchanging P and dP
+//        through LDS.
+// The accumulator of one 32-row block at d = 128 takes 64 VGPRs, so no wave
+// holds two of them.  S and dP are computed twice in all (once for dQ, once
+// for dK and dV): 7 products for the 5 of the definition.
+// Streamed tiles are 32 rows, double-buffered in LDS and loaded into
+// registers one tile ahead.
 //
 // Dropout (DROP): the forward's output was O = (P (.) Z) V / (1 - p), so with
 // f = 1 / (1 - p),  dV = (P (.) Z)^T dO f,  dP = (dO V^T) (.) Z f, and
 // dS = P (.) (dP - D) as before (D = rowsum(dO (.) O) with the dropped O
 // still equals sum_j P dP).  The keep bits Z are the forward's (philox.h).
-// DQ holds one query per lane and keys in its registers, the forward's
-// layout: two generator calls per step give its 16 decisions.  DK and DV
-// hold one key per lane: each lane makes the two calls of one streamed query
-// and one half of the wave's keys, and sixteen wave ballots carry the bits
-// to the lanes of their keys.
+// The dQ kernel holds one query per lane and keys in its registers, the
+// forward's layout: two generator calls per step give its 16 decisions.  In
+// the dK/dV kernel a lane holds one key: each lane makes the two calls of one
+// streamed query and one half of the wave's keys, and sixteen wave ballots
+// carry the bits to the lanes of their keys.
 #include "fa_kernels.h"
 
 #include <stdint.h>
@@ -63,8 +62,6 @@ constexpr int kRows = 32 * kWaves;      // resident rows per workgroup
 static_assert(kRows == kBwdBlockRows, "grid and kernel disagree on the resident tile");
 constexpr int kTile = 32;               // streamed rows per step
 constexpr float kLog2e = 1.4426950408889634f;
-
-enum Mode { kDQ = 0, kDK = 1, kDV = 2 };
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -101,12 +98,11 @@ struct Lay {
 };
 
 // Per-thread staging of one streamed tile: the item (row pair j, chunk c8)
-// of up to two tensors, and one statistic per row for up to two rows.
+// of two tensors.
 template <int D>
 struct Stage {
     u32x4 x0, x1;     // tensor 1, rows 2j and 2j+1
     u32x4 y0, y1;     // tensor 2, rows 2j and 2j+1
-    float s0, s1;     // statistics of row tid (tid < 32)
 };
 
 template <int D>
@@ -176,14 +172,11 @@ __global__ __launch_bounds__(256) void bwd_rowdot_kernel(const __bf16* __restric
     if (row < rows && c == 0) Dout[row] = acc;
 }
 
-// One backward kernel per accumulator (MODE), see the file header.
-//   resident rows: queries (DQ) or keys (DK, DV) of head rh;
-//   streamed rows: keys of K/V head (DQ) or queries of the query heads of the
-//   GQA group (DK, DV).
-// c = scale * log2(e) (signed).  LSE and D are [B, Hq, N] float32.
+// dQ: resident query rows of head hq, streamed key tiles of K/V head
+// hq / group.  c = scale * log2(e) (signed).  LSE and D are [B, Hq, N] float32.
 // DROP: the forward ran with dropout `dr` (see the file header).
-template <int D, bool CAUSAL, int MODE, bool DROP>
-__global__ __launch_bounds__(kThreads, 2) void bwd_kernel(
+template <int D, bool CAUSAL, bool DROP>
+__global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const __bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dd,
     __bf16* __restrict__ G, int Hq, int Hkv, int N, int n_rtiles, int bh_total, float c, float scale,
@@ -191,21 +184,19 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kernel(
     using L = Lay<D>;
     constexpr int KS = D / 16;
     constexpr int DB = D / 32;
-    constexpr bool RES_Q = MODE == kDQ;
 
     __shared__ __attribute__((aligned(16))) char smem_raw[L::BYTES];
     LDS char* smem = (LDS char*)smem_raw;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = lane >> 5;
     const int l32 = lane & 31;
     const int group = Hq / Hkv;
 
     // Work decomposition, XCD-aware as in the forward; for causal attention the
-    // heaviest resident tiles go first (last query tiles for DQ, first key
-    // tiles for DK and DV).
+    // heaviest (last) query tiles go first.
     int bh, rt;
     {
         const int w = blockIdx.x;
@@ -217,37 +208,31 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kernel(
             bh = w / n_rtiles;
             rt = w % n_rtiles;
         }
-        if (CAUSAL && RES_Q) rt = n_rtiles - 1 - rt;
+        if (CAUSAL) rt = n_rtiles - 1 - rt;
     }
-    const int b = bh / (RES_Q ? Hq : Hkv);
-    const int hr = bh % (RES_Q ? Hq : Hkv);             // resident head
+    const int b = bh / Hq;
+    const int hr = bh % Hq;                              // query head
     const int r0 = rt * kRows;                           // first resident row of the workgroup
     const int wr0 = r0 + 32 * wave;                      // first resident row of this wave
-    const int my_row = wr0 + l32;                        // the resident row of this lane
+    const int my_row = wr0 + l32;                        // the resident query of this lane
 
-    // Resident operands (B operand of the score products): lane holds
-    // d = 16*ks + 8*h .. +7 of its row.
-    const size_t rhead = ((size_t)b * (RES_Q ? Hq : Hkv) + hr) * N * D;
+    // Resident Q and dO (B operands of S^T = K Q^T and dP^T = V dO^T): lane
+    // holds d = 16*ks + 8*h .. +7 of its row.
+    const size_t rhead = ((size_t)b * Hq + hr) * N * D;
     bf16x8 rf1[KS], rf2[KS];
     {
-        const __bf16* t1 = RES_Q ? Q : K;
-        const __bf16* t2 = RES_Q ? dO : V;
         const int rr = min(my_row, N - 1);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            u32x4 x = *(const u32x4*)(t1 + rhead + (size_t)rr * D + 16 * ks + 8 * h);
-            if (my_row >= N) x = (u32x4){0u, 0u, 0u, 0u};
+            u32x4 x = *(const u32x4*)(Q + rhead + (size_t)rr * D + 16 * ks + 8 * h);
+            u32x4 y = *(const u32x4*)(dO + rhead + (size_t)rr * D + 16 * ks + 8 * h);
+            if (my_row >= N) x = y = (u32x4){0u, 0u, 0u, 0u};
             rf1[ks] = __builtin_bit_cast(bf16x8, x);
-            if constexpr (MODE != kDV) {
-                u32x4 y = *(const u32x4*)(t2 + rhead + (size_t)rr * D + 16 * ks + 8 * h);
-                if (my_row >= N) y = (u32x4){0u, 0u, 0u, 0u};
-                rf2[ks] = __builtin_bit_cast(bf16x8, y);
-            }
+            rf2[ks] = __builtin_bit_cast(bf16x8, y);
         }
     }
-    // Per-lane statistics of a resident query row (DQ).
-    float lse2_lane = 0.f, d_lane = 0.f;
-    if constexpr (RES_Q) {
+    float lse2_lane, d_lane;
+    {
         const size_t srow = ((size_t)b * Hq + hr) * N + min(my_row, N - 1);
         lse2_lane = LSE[srow] * kLog2e;
         d_lane = Dd[srow];
@@ -257,63 +242,22 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kernel(
 #pragma unroll
     for (int db = 0; db < DB; ++db) acc[db] = (f32x16){};
 
-    // Streamed range.  DQ: key tiles 0 .. (last visible key)/32 of K/V head
-    // hq / group.  DK/DV: for each query head of the group, query tiles from
-    // the first one that can see the workgroup's keys.
-    const int heads = RES_Q ? 1 : group;
-    int t_begin, t_end;
-    if constexpr (RES_Q) {
-        t_begin = 0;
-        t_end = ((CAUSAL ? min(N, r0 + kRows) : N) + kTile - 1) / kTile;
-    } else {
-        t_begin = CAUSAL ? r0 / kTile : 0;
-        t_end = (N + kTile - 1) / kTile;
-    }
-    const int per_head = max(0, t_end - t_begin);
-    const int n_steps = heads * per_head;
+    // Streamed key tiles 0 .. (last visible key)/32 of the K/V head.
+    const int n_steps = ((CAUSAL ? min(N, r0 + kRows) : N) + kTile - 1) / kTile;
+    const size_t kvhead = ((size_t)b * Hkv + hr / group) * N * D;
 
-    auto src_head = [&](int hs) -> size_t {
-        // base element offset of the streamed head: K/V head for DQ, query head for DK/DV
-        if constexpr (RES_Q) return ((size_t)b * Hkv + hr / group) * N * D;
-        else return ((size_t)b * Hq + hr * group + hs) * N * D;
-    };
-    auto stat_base = [&](int hs) -> size_t { return ((size_t)b * Hq + hr * group + hs) * N; };
-
+    // Each step's copy: A = K rows, B = V rows, T = K transposed.
     Stage<D> stg;
     auto load_step = [&](int step) __attribute__((always_inline)) {
-        const int s = min(step, n_steps - 1);
-        const int hs = s / per_head;
-        const int row0 = (t_begin + s % per_head) * kTile;
-        const size_t base = src_head(hs);
-        if constexpr (MODE == kDQ) {
-            stage_rows<D>(K + base, row0, N, tid, stg.x0, stg.x1);
-            stage_rows<D>(V + base, row0, N, tid, stg.y0, stg.y1);
-        } else if constexpr (MODE == kDK) {
-            stage_rows<D>(Q + base, row0, N, tid, stg.x0, stg.x1);
-            stage_rows<D>(dO + base, row0, N, tid, stg.y0, stg.y1);
-            stage_stats(LSE + stat_base(hs), Dd + stat_base(hs), row0, N, tid, stg.s0, stg.s1);
-        } else {
-            stage_rows<D>(Q + base, row0, N, tid, stg.x0, stg.x1);
-            stage_rows<D>(dO + base, row0, N, tid, stg.y0, stg.y1);
-            stage_stats(LSE + stat_base(hs), nullptr, row0, N, tid, stg.s0, stg.s1);
-        }
+        const int row0 = min(step, n_steps - 1) * kTile;
+        stage_rows<D>(K + kvhead, row0, N, tid, stg.x0, stg.x1);
+        stage_rows<D>(V + kvhead, row0, N, tid, stg.y0, stg.y1);
     };
-    // Writes the staged tile into buffer set `set`:
-    //   DQ: A = K rows, B = V rows, T = K transposed;
-    //   DK: A = Q rows, B = dO rows, T = Q transposed, stats = LSE*log2e, D;
-    //   DV: A = Q rows, T = dO transposed, stats = LSE*log2e.
     auto store_step = [&](int set) __attribute__((always_inline)) {
         LDS char* base = smem + set * L::SET;
         put_rows<D>(base + L::A, tid, stg.x0, stg.x1);
-        if constexpr (MODE != kDV) put_rows<D>(base + L::B, tid, stg.y0, stg.y1);
-        if constexpr (MODE == kDV) put_transposed<D>(base + L::T, tid, stg.y0, stg.y1);
-        else put_transposed<D>(base + L::T, tid, stg.x0, stg.x1);
-        if constexpr (MODE != kDQ) {
-            if (tid < kTile) {
-                ((LDS float*)(base + L::S))[tid] = stg.s0;
-                ((LDS float*)(base + L::S))[kTile + tid] = stg.s1;
-            }
-        }
+        put_rows<D>(base + L::B, tid, stg.y0, stg.y1);
+        put_transposed<D>(base + L::T, tid, stg.x0, stg.x1);
     };
 
     if (n_steps > 0) {
@@ -327,143 +271,62 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kernel(
     for (int step = 0; step < n_steps; ++step) {
         const int set = step & 1;
         const LDS char* base = smem + set * L::SET;
-        const int row0 = (t_begin + step % per_head) * kTile;   // first streamed row of the tile
-
-        // Does this wave see any pair of the tile?  (causal only)
+        const int row0 = step * kTile;                          // first key of the tile
+        // Does this wave see any pair of the tile?  (keys row0.. vs queries wr0..wr0+31)
         bool active = wr0 < N;
         bool masked = row0 + kTile > N;
         if (CAUSAL) {
-            if (RES_Q) {   // keys row0.. vs queries wr0..wr0+31
-                active = active && row0 <= wr0 + 31;
-                masked = masked || row0 + kTile - 1 > wr0;
-            } else {       // queries row0.. vs keys wr0..wr0+31
-                active = active && row0 + kTile - 1 >= wr0;
-                masked = masked || row0 < wr0 + 31;
-            }
+            active = active && row0 <= wr0 + 31;
+            masked = masked || row0 + kTile - 1 > wr0;
         }
-        if (!RES_Q) masked = masked || wr0 + 32 > N;
-
         if (active) {
-            // Dropout keep bits of this wave's pairs (the key j of a pair is
-            // 16a + 8b + 4cc + w; its draw is half 4b + w of the call at
-            // counter (2a + cc, query, query head unit, offset)).
-            //   DQ: lane = query my_row, register i = key row0 + 16(i/8) +
-            //       8((i/4)%2) + 4h + i%4: call i/8 at counter 2(row0/16 + i/8) + h
-            //       holds register i's draw in half i%8.
-            //   DK, DV: zword bit r = keep bit of (query row0 + 4h + r, my key).
+            // Dropout keep bits: lane = query my_row, register i = key row0 +
+            // 16(i/8) + 8((i/4)%2) + 4h + i%4; call i/8 at counter
+            // 2(row0/16 + i/8) + h holds register i's draw in half i%8.
             uint32_t kw[2][4];
-            uint32_t zword = 0;
             if constexpr (DROP) {
-                const uint32_t t = dr.t2 & 0xFFFFu;
                 // The empty asm hides which counter and key words stay fixed
                 // over the steps; otherwise the optimiser keeps partial rounds
-                // and the ten round keys live across the loop (and spills them).
+                // and the ten round keys live across the loop.
                 uint32_t k0 = dr.k0, k1 = dr.k1;
                 asm volatile("" : "+s"(k0), "+s"(k1));
-                if constexpr (RES_Q) {
-                    uint32_t row_u = (uint32_t)my_row;
-                    asm volatile("" : "+v"(row_u));
+                uint32_t row_u = (uint32_t)my_row;
+                asm volatile("" : "+v"(row_u));
 #pragma unroll
-                    for (int a2 = 0; a2 < 2; ++a2) {
-                        const PhiloxOut r = philox4x32_10((uint32_t)(2 * ((row0 >> 4) + a2) + h), row_u,
-                                                          (uint32_t)bh, dr.offset, k0, k1);
+                for (int a2 = 0; a2 < 2; ++a2) {
+                    const PhiloxOut r = philox4x32_10((uint32_t)(2 * ((row0 >> 4) + a2) + h), row_u, (uint32_t)bh,
+                                                      dr.offset, k0, k1);
 #pragma unroll
-                        for (int m = 0; m < 4; ++m) kw[a2][m] = r.w[m];
-                    }
-                } else {
-                    // Lane (l32, h) draws for query row0 + l32 and the keys
-                    // wr0 + 16al + 4h + {0..3, 8..11}: bit 8al + k of `mine`
-                    // is half k of call al.
-                    const uint32_t bhq = (uint32_t)(b * Hq + hr * group + step / per_head);
-                    uint32_t mine = 0;
-                    uint32_t ctr0 = (uint32_t)(2 * (wr0 >> 4) + h);
-                    asm volatile("" : "+v"(ctr0));
-#pragma unroll
-                    for (int al = 0; al < 2; ++al) {
-                        const PhiloxOut r = philox4x32_10(ctr0 + 2 * al,
-                                                          (uint32_t)(row0 + l32), bhq, dr.offset, k0, k1);
-#pragma unroll
-                        for (int k = 0; k < 8; ++k)
-                            mine |= (uint32_t)keep_half(r.w[k >> 1], k & 1, t) << (8 * al + k);
-                    }
-                    // My key wr0 + l32 is bit pos of the lanes whose h equals
-                    // its bit 2: lane l32' + 32 * that bit holds query l32'.
-                    // The selection is arithmetic (one-hot `sel`, shift `sh`),
-                    // and the asm keeps the optimiser from hoisting sixteen
-                    // loop-invariant masks out of the step loop.
-                    const int pos = ((l32 >> 4) << 3) | (((l32 >> 3) & 1) << 2) | (l32 & 3);
-                    uint32_t sel = 1u << pos;
-                    uint32_t sh = ((l32 >> 2) & 1) * 32u;
-                    asm volatile("" : "+v"(sel), "+v"(sh));
-#pragma unroll
-                    for (int bit = 0; bit < 16; ++bit) {
-                        const uint64_t bal = __builtin_amdgcn_ballot_w64((mine >> bit) & 1u);
-                        zword |= (uint32_t)(bal >> sh) & (0u - ((sel >> bit) & 1u));
-                    }
-                    // Register i's query is (i/4)*8 + 4h + i%4: shift out 4h
-                    // here so that the per-element shifts are immediates (a
-                    // per-lane shift count per element would be 16 registers
-                    // kept across the loop).
-                    zword >>= 4 * h;
+                    for (int m = 0; m < 4; ++m) kw[a2][m] = r.w[m];
                 }
             }
-            // score products: X = A_tile (rows) x resident^T, one resident row per lane
+            // score products: S^T and dP^T with one query per lane
             const LDS char* arow = base + L::A + l32 * L::RPITCH + 16 * h;
-            f32x16 x = (f32x16){};
+            const LDS char* brow = base + L::B + l32 * L::RPITCH + 16 * h;
+            f32x16 x = (f32x16){}, y = (f32x16){};
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
+            for (int ks = 0; ks < KS; ++ks) {
                 x = mfma32(*(const LDS bf16x8*)(arow + 32 * ks), rf1[ks], x);
-            f32x16 y = (f32x16){};
-            if constexpr (MODE != kDV) {
-                const LDS char* brow = base + L::B + l32 * L::RPITCH + 16 * h;
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks)
-                    y = mfma32(*(const LDS bf16x8*)(brow + 32 * ks), rf2[ks], y);
+                y = mfma32(*(const LDS bf16x8*)(brow + 32 * ks), rf2[ks], y);
             }
-            // register i holds streamed row sr(i) = (i/4)*8 + 4*h + i%4 of the tile;
-            // the statistics of rows 8g + 4h .. +3 are one 16-byte LDS read
-            const LDS float* st = (const LDS float*)(base + L::S);
-            f32x4 lse4[4], d4[4];
-            if constexpr (!RES_Q) {
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    lse4[g] = *(const LDS f32x4*)(st + 8 * g + 4 * h);
-                    if constexpr (MODE == kDK) d4[g] = *(const LDS f32x4*)(st + kTile + 8 * g + 4 * h);
-                }
-            }
+            // register i holds key row0 + (i/4)*8 + 4h + i%4
             bf16x8 w[2];
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const int sr = (i >> 2) * 8 + 4 * h + (i & 3);
-                const int srow = row0 + sr;
-                float lse2, dv;
-                int key, qry;
-                if constexpr (RES_Q) {
-                    lse2 = lse2_lane;
-                    dv = d_lane;
-                    key = srow;
-                    qry = my_row;
-                } else {
-                    lse2 = lse4[i >> 2][i & 3];
-                    dv = MODE == kDK ? d4[i >> 2][i & 3] : 0.f;
-                    key = my_row;
-                    qry = srow;
-                }
+                const int key = row0 + (i >> 2) * 8 + 4 * h + (i & 3);
                 bool dead = false;
-                if (masked) dead = key >= N || qry >= N || (CAUSAL && key > qry);
-                const float p = dead ? 0.f : __builtin_amdgcn_exp2f(fmaf(x[i], c, -lse2));
-                bool kept = true;
-                if constexpr (DROP) {
-                    if constexpr (RES_Q) kept = keep_half(kw[i >> 3][(i & 7) >> 1], i & 1, dr.t2 & 0xFFFFu);
-                    else kept = (zword >> ((i >> 2) * 8 + (i & 3))) & 1u;
-                }
+                if (masked) dead = key >= N || my_row >= N || (CAUSAL && key > my_row);
+                const float p = dead ? 0.f : __builtin_amdgcn_exp2f(fmaf(x[i], c, -lse2_lane));
                 float val;
-                if constexpr (MODE == kDV) val = kept ? p : 0.f;              // times f in the epilogue
-                else if constexpr (DROP) val = p * ((kept ? y[i] * dr.factor : 0.f) - dv);
-                else val = p * (y[i] - dv);
+                if constexpr (DROP) {
+                    const bool kept = keep_half(kw[i >> 3][(i & 7) >> 1], i & 1, dr.t2 & 0xFFFFu);
+                    val = p * ((kept ? y[i] * dr.factor : 0.f) - d_lane);
+                } else {
+                    val = p * (y[i] - d_lane);
+                }
                 w[i >> 3][i & 7] = (__bf16)val;
             }
-            // accumulator product: acc^T (d x resident) += T_tile^T (d x streamed) w
+            // dQ^T (d x queries) += (K^T) (d x keys) dS^T
             const LDS char* trow = base + L::T + l32 * L::TPITCH + 16 * h;
 #pragma unroll
             for (int db = 0; db < DB; ++db)
@@ -477,10 +340,268 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kernel(
         if (step + 2 < n_steps) load_step(step + 2);
     }
 
-    // Epilogue: this lane's resident row, d = 32*db + 8*g + 4*h + r.
+    // Epilogue: this lane's query row, d = 32*db + 8*g + 4*h + r.
     if (my_row >= N) return;
-    const float f = MODE == kDV ? (DROP ? dr.factor : 1.f) : scale;
     __bf16* gp = G + rhead + (size_t)my_row * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            bf16x4 out;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) out[r] = (__bf16)(acc[db][4 * g + r] * scale);
+            *(bf16x4*)(gp + 32 * db + 8 * g + 4 * h) = out;
+        }
+}
+
+// dK and dV in one launch.  A workgroup of 8 waves holds 128 resident keys,
+// 32 per wave pair (wave w and w + 4), and streams the query tiles of the
+// GQA group once for both waves of every pair.  Per 32-row step:
+//   first half:  wave w     S = Q K^T (8 MFMAs), P (exp), P out to LDS;
+//                wave w+4   dP = dO V^T (8 MFMAs), dP out to LDS;
+//   barrier;
+//   second half: wave w     dS = P (.) (dP - D), dK^T += Q^T dS (8 MFMAs);
+//                wave w+4   dV^T += dO^T P (8 MFMAs);  next tile to LDS;
+//   barrier.
+// So each SIMD (one wave of each kind) has 16 MFMAs in each half, and S and
+// dP are computed once per pair (the separate DK and DV kernels computed S
+// twice and streamed Q and dO twice).  P goes over in bf16 (it is rounded so
+// for the products anyway, thinned by dropout); dP in fp32.
+template <int D>
+struct Lay2 {
+    static constexpr int RPITCH = 2 * D + 16;
+    static constexpr int TPITCH = 2 * kTile + 16;
+    static constexpr int RBYTES = kTile * RPITCH;
+    static constexpr int TBYTES = D * TPITCH;
+    static constexpr int A = 0;                           // Q rows
+    static constexpr int B = RBYTES;                      // dO rows
+    static constexpr int TQ = 2 * RBYTES;                 // Q^T
+    static constexpr int TO = 2 * RBYTES + TBYTES;        // dO^T
+    static constexpr int S = 2 * RBYTES + 2 * TBYTES;     // LSE*log2e and D of the 32 rows
+    static constexpr int SET = S + 2 * kTile * 4;
+    static constexpr int PXP = 2 * SET;                   // P:  [4 pairs][2 chunks][64 lanes] x 16 B
+    static constexpr int PXD = PXP + 4 * 2 * 64 * 16;     // dP: [4 pairs][4 quads][64 lanes] x 16 B
+    static constexpr int BYTES = PXD + 4 * 4 * 64 * 16;
+    static constexpr int ITEMS = (kTile / 2) * (D / 8);
+};
+constexpr int kDkvThreads = 512;
+
+template <int D, bool CAUSAL, bool DROP>
+__global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(
+    const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
+    const __bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dd,
+    __bf16* __restrict__ dK, __bf16* __restrict__ dV, int Hq, int Hkv, int N, int n_rtiles, int bh_total,
+    float c, float scale, Dropout dr) {
+    using L = Lay2<D>;
+    constexpr int KS = D / 16;
+    constexpr int DB = D / 32;
+
+    __shared__ __attribute__((aligned(16))) char smem_raw[L::BYTES];
+    LDS char* smem = (LDS char*)smem_raw;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    // (readfirstlane: the wave index is uniform, so the role and block tests
+    // below become scalar branches)
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool dk_role = wave < 4;            // waves 0-3: S, P, dS, dK; waves 4-7: dP, dV
+    const int wb = wave & 3;                  // resident block of the wave pair
+    const int h = lane >> 5;
+    const int l32 = lane & 31;
+    const int group = Hq / Hkv;
+
+    int bh, rt;
+    {
+        const int w = blockIdx.x;
+        if ((bh_total & 7) == 0) {
+            const int slot = w >> 3;
+            bh = (w & 7) * (bh_total >> 3) + slot % (bh_total >> 3);
+            rt = slot / (bh_total >> 3);
+        } else {
+            bh = w / n_rtiles;
+            rt = w % n_rtiles;
+        }
+    }
+    const int b = bh / Hkv;
+    const int hr = bh % Hkv;                  // K/V head
+    const int r0 = rt * kRows;
+    const int wr0 = r0 + 32 * wb;
+    const int my_row = wr0 + l32;             // this lane's key
+    const size_t rhead = ((size_t)b * Hkv + hr) * N * D;
+
+    // resident rows: K for the S waves, V for the dP waves (B operands)
+    bf16x8 rf[KS];
+    {
+        const int rr = min(my_row, N - 1);
+        const __bf16* src = (dk_role ? K : V) + rhead + (size_t)rr * D;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            u32x4 x = *(const u32x4*)(src + 16 * ks + 8 * h);
+            if (my_row >= N) x = (u32x4){0u, 0u, 0u, 0u};
+            rf[ks] = __builtin_bit_cast(bf16x8, x);
+        }
+    }
+    f32x16 acc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc[db] = (f32x16){};
+
+    const int t_begin = CAUSAL ? r0 / kTile : 0;
+    const int t_end = (N + kTile - 1) / kTile;
+    const int per_head = max(0, t_end - t_begin);
+    const int n_steps = group * per_head;
+    auto q_head = [&](int hs) -> size_t { return ((size_t)b * Hq + hr * group + hs) * N; };
+
+    // Copies: threads 0-255 stage Q rows, 256-511 dO rows (item it = tid & 255),
+    // threads 0-31 also the row statistics.
+    const int ct = tid & 255;
+    const bool copy_do = tid >= 256;
+    u32x4 x0, x1;
+    float s0 = 0.f, s1 = 0.f;
+    auto load_step = [&](int step) __attribute__((always_inline)) {
+        const int st = min(step, n_steps - 1);
+        const int hs = st / per_head;
+        const int row0 = (t_begin + st % per_head) * kTile;
+        stage_rows<D>((copy_do ? dO : Q) + q_head(hs) * D, row0, N, ct, x0, x1);
+        if (tid < kTile) stage_stats(LSE + q_head(hs), Dd + q_head(hs), row0, N, tid, s0, s1);
+    };
+    auto store_step = [&](int set) __attribute__((always_inline)) {
+        LDS char* base = smem + set * L::SET;
+        put_rows<D>(base + (copy_do ? L::B : L::A), ct, x0, x1);
+        put_transposed<D>(base + (copy_do ? L::TO : L::TQ), ct, x0, x1);
+        if (tid < kTile) {
+            ((LDS float*)(base + L::S))[tid] = s0;
+            ((LDS float*)(base + L::S))[kTile + tid] = s1;
+        }
+    };
+
+    if (n_steps > 0) {
+        load_step(0);
+        store_step(0);
+        load_step(1);
+    }
+    __syncthreads();
+
+    LDS bf16x8* pxp = (LDS bf16x8*)(smem + L::PXP) + wb * 128;   // [cc][lane]
+    LDS f32x4* pxd = (LDS f32x4*)(smem + L::PXD) + wb * 256;     // [quad][lane]
+
+#pragma unroll 1
+    for (int step = 0; step < n_steps; ++step) {
+        const int set = step & 1;
+        const LDS char* base = smem + set * L::SET;
+        const int row0 = (t_begin + step % per_head) * kTile;
+        bool active = wr0 < N;
+        bool masked = row0 + kTile > N || wr0 + 32 > N;
+        if (CAUSAL) {
+            active = active && row0 + kTile - 1 >= wr0;
+            masked = masked || row0 < wr0 + 31;
+        }
+        // register i of a 32x32 accumulator: streamed row (i/4)*8 + 4h + i%4 of the
+        // tile (a query), resident key my_row (the lane)
+        float p[16];
+        uint32_t zword = 0;
+        if (active) {
+            const LDS char* srow = base + (dk_role ? L::A : L::B) + l32 * L::RPITCH + 16 * h;
+            f32x16 x = (f32x16){};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) x = mfma32(*(const LDS bf16x8*)(srow + 32 * ks), rf[ks], x);
+            if (!dk_role) {            // dP out
+#pragma unroll
+                for (int qd = 0; qd < 4; ++qd)
+                    pxd[qd * 64 + lane] = (f32x4){x[4 * qd], x[4 * qd + 1], x[4 * qd + 2], x[4 * qd + 3]};
+            } else {                   // P (and the dropout bits), P out
+                if constexpr (DROP) {
+                    const uint32_t t = dr.t2 & 0xFFFFu;
+                    // the key (and so its ten round keys) and the multipliers in
+                    // vector registers: this kernel's scalar registers are nearly
+                    // all taken
+                    uint32_t k0 = dr.k0, k1 = dr.k1, m0 = kPhiloxM0, m1 = kPhiloxM1;
+                    asm volatile("" : "+v"(k0), "+v"(k1), "+v"(m0), "+v"(m1));
+                    const uint32_t bhq = (uint32_t)(b * Hq + hr * group + step / per_head);
+                    uint32_t mine = 0;
+                    uint32_t ctr0 = (uint32_t)(2 * (wr0 >> 4) + h);
+                    asm volatile("" : "+v"(ctr0));
+#pragma unroll
+                    for (int al = 0; al < 2; ++al) {
+                        const PhiloxOut r =
+                            philox4x32_10(ctr0 + 2 * al, (uint32_t)(row0 + l32), bhq, dr.offset, k0, k1, m0, m1);
+#pragma unroll
+                        for (int k = 0; k < 8; ++k)
+                            mine |= (uint32_t)keep_half(r.w[k >> 1], k & 1, t) << (8 * al + k);
+                    }
+                    const int pos = ((l32 >> 4) << 3) | (((l32 >> 3) & 1) << 2) | (l32 & 3);
+                    uint32_t sel = 1u << pos;
+                    uint32_t sh = ((l32 >> 2) & 1) * 32u;
+                    asm volatile("" : "+v"(sel), "+v"(sh));
+#pragma unroll
+                    for (int bit = 0; bit < 16; ++bit) {
+                        const uint64_t bal = __builtin_amdgcn_ballot_w64((mine >> bit) & 1u);
+                        zword |= (uint32_t)(bal >> sh) & (0u - ((sel >> bit) & 1u));
+                    }
+                    zword >>= 4 * h;
+                }
+                const LDS float* st = (const LDS float*)(base + L::S);
+                bf16x8 pw[2];
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const f32x4 lse4 = *(const LDS f32x4*)(st + 8 * g + 4 * h);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int i = 4 * g + e;
+                        const int qry = row0 + 8 * g + 4 * h + e;
+                        bool dead = false;
+                        if (masked) dead = my_row >= N || qry >= N || (CAUSAL && my_row > qry);
+                        p[i] = dead ? 0.f : __builtin_amdgcn_exp2f(fmaf(x[i], c, -lse4[e]));
+                        // keep bit as a 0/1 multiplier (no condition registers held)
+                        const float keepf = DROP ? (float)((zword >> (8 * g + e)) & 1u) : 1.f;
+                        pw[i >> 3][i & 7] = (__bf16)(p[i] * keepf);
+                    }
+                }
+                pxp[lane] = pw[0];
+                pxp[64 + lane] = pw[1];
+            }
+        }
+        __syncthreads();
+        if (active) {
+            bf16x8 w[2];
+            if (dk_role) {             // dS from the partner's dP
+                const LDS float* st = (const LDS float*)(base + L::S);
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const f32x4 dp = pxd[g * 64 + lane];
+                    const f32x4 d4 = *(const LDS f32x4*)(st + kTile + 8 * g + 4 * h);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int i = 4 * g + e;
+                        float val;
+                        if constexpr (DROP) {
+                            const float keepf = (float)((zword >> (8 * g + e)) & 1u) * dr.factor;
+                            val = p[i] * fmaf(dp[e], keepf, -d4[e]);
+                        } else {
+                            val = p[i] * (dp[e] - d4[e]);
+                        }
+                        w[i >> 3][i & 7] = (__bf16)val;
+                    }
+                }
+            } else {                   // P from the partner
+                w[0] = pxp[lane];
+                w[1] = pxp[64 + lane];
+            }
+            // dK^T += (Q^T) dS  or  dV^T += (dO^T) P
+            const LDS char* trow = base + (dk_role ? L::TQ : L::TO) + l32 * L::TPITCH + 16 * h;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int cc = 0; cc < 2; ++cc)
+                    acc[db] = mfma32(*(const LDS bf16x8*)(trow + 32 * db * L::TPITCH + 32 * cc), w[cc], acc[db]);
+        }
+        if (step + 1 < n_steps) store_step(set ^ 1);
+        __syncthreads();
+        if (step + 2 < n_steps) load_step(step + 2);
+    }
+
+    if (my_row >= N) return;
+    const float f = dk_role ? scale : (DROP ? dr.factor : 1.f);
+    __bf16* gp = (dk_role ? dK : dV) + rhead + (size_t)my_row * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -492,10 +613,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kernel(
         }
 }
 
-template <int D, bool CAUSAL, int MODE, bool DROP>
-hipError_t launch_mode(const BwdArgs& a, const float* dd, const Dropout& drop, hipStream_t stream) {
+template <int D, bool CAUSAL, bool DROP>
+hipError_t launch_dkv(const BwdArgs& a, const float* dd, const Dropout& drop, hipStream_t stream) {
     int n_rtiles = (a.N + kRows - 1) / kRows;
-    int bh_total = a.B * (MODE == kDQ ? a.Hq : a.Hkv);
+    int bh_total = a.B * a.Hkv;
     float c = a.scale * kLog2e;
     float scale = a.scale;
     int Hq = a.Hq, Hkv = a.Hkv, N = a.N;
@@ -504,11 +625,32 @@ hipError_t launch_mode(const BwdArgs& a, const float* dd, const Dropout& drop, h
     const __bf16* v = (const __bf16*)a.v;
     const __bf16* dO = (const __bf16*)a.dO;
     const float* lse = a.lse;
-    __bf16* g = (__bf16*)(MODE == kDQ ? a.dq : MODE == kDK ? a.dk : a.dv);
+    __bf16* gk = (__bf16*)a.dk;
+    __bf16* gv = (__bf16*)a.dv;
+    Dropout dr = drop;
+    void* args[] = {(void*)&q, (void*)&k, (void*)&v, (void*)&dO, (void*)&lse, (void*)&dd, &gk, &gv,
+                    &Hq, &Hkv, &N, &n_rtiles, &bh_total, &c, &scale, &dr};
+    return hipLaunchKernel((const void*)bwd_dkv_kernel<D, CAUSAL, DROP>, dim3(bh_total * n_rtiles),
+                           dim3(kDkvThreads), args, 0, stream);
+}
+
+template <int D, bool CAUSAL, bool DROP>
+hipError_t launch_dq(const BwdArgs& a, const float* dd, const Dropout& drop, hipStream_t stream) {
+    int n_rtiles = (a.N + kRows - 1) / kRows;
+    int bh_total = a.B * a.Hq;
+    float c = a.scale * kLog2e;
+    float scale = a.scale;
+    int Hq = a.Hq, Hkv = a.Hkv, N = a.N;
+    const __bf16* q = (const __bf16*)a.q;
+    const __bf16* k = (const __bf16*)a.k;
+    const __bf16* v = (const __bf16*)a.v;
+    const __bf16* dO = (const __bf16*)a.dO;
+    const float* lse = a.lse;
+    __bf16* g = (__bf16*)a.dq;
     Dropout dr = drop;
     void* args[] = {(void*)&q, (void*)&k, (void*)&v, (void*)&dO, (void*)&lse, (void*)&dd, &g,
                     &Hq, &Hkv, &N, &n_rtiles, &bh_total, &c, &scale, &dr};
-    return hipLaunchKernel((const void*)bwd_kernel<D, CAUSAL, MODE, DROP>, dim3(bh_total * n_rtiles),
+    return hipLaunchKernel((const void*)bwd_dq_kernel<D, CAUSAL, DROP>, dim3(bh_total * n_rtiles),
                            dim3(kThreads), args, 0, stream);
 }
 
@@ -524,9 +666,8 @@ hipError_t launch_all(const BwdArgs& a, float* workspace, const Dropout& dr, hip
                                    dim3((unsigned)((rows + per_block - 1) / per_block)), dim3(256), args,
                                    0, stream);
     if (e != hipSuccess) return e;
-    if ((e = launch_mode<D, CAUSAL, kDQ, DROP>(a, dd, dr, stream)) != hipSuccess) return e;
-    if ((e = launch_mode<D, CAUSAL, kDK, DROP>(a, dd, dr, stream)) != hipSuccess) return e;
-    return launch_mode<D, CAUSAL, kDV, DROP>(a, dd, dr, stream);
+    if ((e = launch_dq<D, CAUSAL, DROP>(a, dd, dr, stream)) != hipSuccess) return e;
+    return launch_dkv<D, CAUSAL, DROP>(a, dd, dr, stream);
 }
 
 }  // namespace

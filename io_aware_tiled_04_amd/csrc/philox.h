@@ -35,16 +35,19 @@ constexpr uint32_t kPhiloxW1 = 0xBB67AE85u;
 // 2 with the two multipliers; the new state is (hi(M1 c2) ^ c1 ^ k0,
 // lo(M1 c2), hi(M0 c0) ^ c3 ^ k1, lo(M0 c0)).  The key grows by the Weyl
 // increments before every round after the first.
+// (m0, m1: the two multipliers, passed in so that a kernel short of scalar
+// registers can hold them in vector registers.)
 __device__ __forceinline__ PhiloxOut philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
-                                                   uint32_t k0, uint32_t k1) {
+                                                   uint32_t k0, uint32_t k1, uint32_t m0 = kPhiloxM0,
+                                                   uint32_t m1 = kPhiloxM1) {
 #pragma unroll
     for (int r = 0; r < 10; ++r) {
         if (r) {
             k0 += kPhiloxW0;
             k1 += kPhiloxW1;
         }
-        const uint64_t p0 = (uint64_t)kPhiloxM0 * c0;
-        const uint64_t p1 = (uint64_t)kPhiloxM1 * c2;
+        const uint64_t p0 = (uint64_t)m0 * c0;
+        const uint64_t p1 = (uint64_t)m1 * c2;
         const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
         const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
         c1 = (uint32_t)p1;

@@ -1,11 +1,13 @@
-"""Every kernel compiles for gfx950 without register spills (CPU only).
+"""Every kernel compiles for gfx950 without spilling to memory (CPU only).
 
-A spill sends registers to scratch memory, which costs the matrix phases far
-more than the spilled registers are worth; it has happened before when a
+A VGPR spill sends registers to scratch memory, which costs the matrix
+phases far more than the spilled registers are worth; it has happened when a
 change pushed one instance of a kernel template past 256 VGPRs.  This test
 compiles each HIP source with the compiler's resource report and checks
-every kernel instance, and that the forward and backward kernels keep two
-waves per SIMD.
+every kernel instance: no VGPR spills, no scratch memory at all, and two
+waves per SIMD for the forward and backward kernels.  SGPR spills are
+allowed: they go to lanes of a VGPR (v_writelane / v_readlane), not to
+memory, and the scratch check would catch any that did not.
 """
 import os
 import re
@@ -18,7 +20,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "io_aware_tiled_04_amd", "csrc")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["fa_fwd_bf16.hip", "fa_fwd_f32.hip", "fa_bwd_bf16.hip"]
+SOURCES = ["fa_fwd_bf16.hip", "fa_fwd_f32.hip", "fa_bwd_bf16.hip", "fa_fwd_kvouter.hip"]
 
 
 def _report(src, tmp_path):
@@ -49,6 +51,6 @@ def test_no_spills_and_occupancy(src, tmp_path):
     assert kernels, f"no kernel resource report for {src}"
     for name, r in kernels.items():
         assert r.get("VGPRs Spill", 0) == 0, (name, r)
-        assert r.get("SGPRs Spill", 0) == 0, (name, r)
-        if "fwd_bf16_kernel" in name or "bwd_kernel" in name:
+        assert r.get("ScratchSize [bytes/lane]", 0) == 0, (name, r)
+        if "fwd_bf16_kernel" in name or "bwd_dq_kernel" in name or "bwd_dkv_kernel" in name:
             assert r.get("Occupancy [waves/SIMD]", 0) >= 2, (name, r)
