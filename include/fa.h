@@ -58,7 +58,7 @@ extern "C" {
 enum fa_status {
     FA_OK = 0,
     FA_ERR_NULL = -1,      /* a null pointer argument (lse included) */
-    FA_ERR_SHAPE = -2,     /* B, Hq, Hkv or N <= 0, or the problem is too large to index */
+    FA_ERR_SHAPE = -2,     /* B, Hq, Hkv or N <= 0, N > 2^23, or the problem is too large to index */
     FA_ERR_HEADS = -3,     /* Hq is not a multiple of Hkv */
     FA_ERR_HEADDIM = -4,   /* d is not one of the supported head sizes (64, 128) */
     FA_ERR_ARG = -5,       /* scale is not finite, num_splits or p_drop is out of range */

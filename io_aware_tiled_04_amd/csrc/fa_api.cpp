@@ -14,7 +14,7 @@ namespace {
 int validate(const void* q, const void* k, const void* v, const void* o, const void* lse, int B,
              int Hq, int Hkv, int N, int d, float scale) {
     if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
-    if (B <= 0 || Hq <= 0 || Hkv <= 0 || N <= 0) return FA_ERR_SHAPE;
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || N <= 0 || N > fa::kMaxSeqLen) return FA_ERR_SHAPE;
     // Every grid must fit one launch dimension (the fp32 kernel has the
     // smallest query tile), and every tensor must be indexable in 64 bits
     // with room to spare (elements < 2^50).

@@ -27,11 +27,12 @@
 //    fed by one group while the other keeps the vector ALUs busy.  K tiles
 //    run one tile ahead of V tiles through LDS to fit this order.  A wave
 //    raises its issue priority for its matrix phase.
-//  * Copies by the vector phase.  The matrix phase reads one 16-byte LDS
-//    operand per MFMA, about as fast as one wave can read LDS, so every
-//    other LDS access in that phase slows it.  The second group therefore
-//    copies K tiles and the first group V tiles, each writing to LDS only in
-//    its own vector phase.
+//  * Direct global-to-LDS copies.  K and V tiles go from HBM straight into
+//    LDS (buffer loads with the LDS flag, no registers, no LDS store
+//    instructions): the second group loads K tiles and the first group V
+//    tiles, each at the end of its matrix phase, into buffer rings deep
+//    enough that the target is free.  Rows past the end of the sequence come
+//    back as zeros from the buffer range check.
 // and one change against a literal reading, exact in real arithmetic:
 //  * Lazy rescaling.  The reference max m of a row is the exact row max of
 //    the first tile; afterwards P is taken against it directly, and m only
@@ -48,11 +49,9 @@
 //  * The S^T accumulator registers 8c..8c+7 of a 32-key block are exactly the
 //    B operand (P^T, 16 keys x 32 queries) of the P V product for the 16-key
 //    chunk c, once the keys of that chunk are taken in the order
-//    {16c+4h+0..3, 16c+8+4h+0..3} for lane half h.  V is stored in LDS
-//    transposed (V^T[d][key]) with the keys of each 16-key chunk permuted into
-//    that order, so one 16-byte LDS read per lane gives the V^T operand of an
-//    MFMA and P never leaves registers.  (An LDS read costs a wave about the
-//    same issue time whatever its width, so the wide reads matter.)
+//    {16c+4h+0..3, 16c+8+4h+0..3} for lane half h, so P never leaves
+//    registers.  V stays row-major in LDS, and two transposing LDS reads
+//    (ds_read_b64_tr_b16) per MFMA give the V^T operand in that key order.
 //  * The O^T accumulator also has one query per lane, so the rescale and the
 //    final 1/l are one multiplier per lane.
 #include "fa_kernels.h"
@@ -82,33 +81,74 @@ constexpr float kSumLimit = 1048576.0f;          // 2^20: largest row sum of a t
 constexpr int kMatrixPrio = 3;                   // wave issue priority during a matrix phase
 // s_getreg immediate for HW_REG_HW_ID (id 4), bits [5:4] = SIMD id
 constexpr int kGetregSimdId = 4 | (4 << 6) | ((2 - 1) << 11);
+// s_waitcnt immediates (vmcnt [3:0] and [15:14], expcnt [6:4], lgkmcnt
+// [11:8]): wait for all vector memory operations, or for all LDS ones.
+constexpr int kWaitVm0 = 0x0F70;
+constexpr int kWaitLgkm0 = 0xC07F;
 
-// K/V tile geometry in LDS: two K buffers ([key][d]) and two V^T buffers
-// ([d][permuted key]).  Row pitches are padded so that the 16-byte operand
-// reads, 32 consecutive rows by 32 lanes, are free of bank conflicts (pitch =
-// 16 mod 256 bytes for both).
+// Workgroup barrier for the tile loop: this wave's LDS reads and writes are
+// complete (lgkmcnt), then s_barrier; the empty asm statements keep the
+// compiler from moving memory accesses across it.  Unlike __syncthreads it
+// does not wait for outstanding vector memory operations: the direct K
+// loads of one phase are meant to land during the next one, and their
+// writer waits for them (vmcnt) before the barrier that publishes the tile.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// K/V tile geometry in LDS: three K buffers and two V buffers, all filled
+// by direct global-to-LDS loads (one wave instruction writes 1 KiB: 16 bytes
+// per lane, in lane order).
+//  * K is stored chunk-major: the 16-byte chunk c (d = 8c .. 8c+7) of key r
+//    sits in slot c * BC + r.  One direct load fills one chunk of all 64
+//    keys, and the S operand read of 32 lanes (32 consecutive keys, one
+//    chunk) is 512 contiguous bytes, free of bank conflicts.
+//  * V is stored row-major ([key][d], 2D bytes per key), with the 16-byte
+//    chunks of key r permuted: chunk c sits at position c ^ vswz(r).  The
+//    P V operand is read with transposing 8-byte reads (ds_read_b64_tr_b16);
+//    a half wave's read covers 4 consecutive keys x 64 bytes, and the
+//    permutation puts those 4 rows on disjoint banks.
 template <int D>
 struct Tile {
     static constexpr int BC = 64;                 // keys per tile
     static constexpr int KB = BC / 32;            // 32-key blocks per tile
-    static constexpr int KPITCH = 2 * D + 16;
-    static constexpr int VPITCH = 2 * BC + 16;    // V^T row: the tile's keys of one d
-    static constexpr int KBYTES = BC * KPITCH;
-    static constexpr int VBYTES = D * VPITCH;
-    static constexpr int K0 = 0, K1 = KBYTES, V0 = 2 * KBYTES, V1 = 2 * KBYTES + VBYTES;
-    static constexpr int ROLE = 2 * (KBYTES + VBYTES);      // 16 ints for the wave roles
+    static constexpr int ROW_CHUNKS = D / 8;      // 16-byte chunks per row
+    static constexpr int KBYTES = BC * D * 2;
+    static constexpr int VBYTES = BC * D * 2;
+    static constexpr int NKBUF = 3;               // K ring: tile t in buffer t % 3
+    static constexpr int V0 = NKBUF * KBYTES, V1 = V0 + VBYTES;
+    static constexpr int ROLE = V1 + VBYTES;      // 16 ints for the wave roles
     static constexpr int LDS_BYTES = ROLE + 64;
-    static constexpr int ROW_CHUNKS = D / 8;       // 16-byte chunks per row
-    // One wave group (kGroupThreads threads) copies a whole K or V tile:
-    // K as 16-byte row chunks, V as (key pair, 8-wide d chunk) items of two
-    // 16-byte loads; both come to STAGE 16-byte registers per thread.
-    static constexpr int K_CHUNKS = BC * ROW_CHUNKS / kGroupThreads;
-    static constexpr int V_ITEMS = (BC / 2) * (D / 8) / kGroupThreads;
-    static constexpr int STAGE = K_CHUNKS;
-    static_assert(BC * ROW_CHUNKS % kGroupThreads == 0 && (BC / 2) * (D / 8) % kGroupThreads == 0,
-                  "tiles must split evenly over a wave group");
-    static_assert(2 * V_ITEMS == K_CHUNKS, "K and V copies use the same staging registers");
+    // Direct loads per wave: the K group's 4 waves load a K tile (ROW_CHUNKS
+    // loads), the V group's 4 waves a V tile (VBYTES / 1024 loads of V_ROWS
+    // whole keys each).
+    static constexpr int K_DMA = ROW_CHUNKS / 4;
+    static constexpr int V_ROWS = 1024 / (2 * D);
+    static constexpr int V_DMA = VBYTES / 1024 / 4;
+    static_assert(BC == 64, "a direct K load covers one chunk of 64 keys");
+    static_assert(ROW_CHUNKS % 4 == 0 && (VBYTES / 1024) % 4 == 0, "tiles must split evenly over a wave group");
 };
+
+// Chunk permutation of V row r (in 16-byte chunks).  The transposing read of
+// a half wave touches rows r0 .. r0+3 (r0 a multiple of 4) at the same 64
+// bytes of the row; with 2D-byte rows these must land on 4 different 64-byte
+// bank groups of the 256-byte bank space.
+template <int D>
+__device__ __forceinline__ int vswz(int r) {
+    static_assert(D == 64 || D == 128, "head dimension");
+    return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
+}
+
+// Buffer descriptor of a raw byte range: loads at or past `bytes` return
+// zeros (the descriptor's range check), which is what the tile copies use
+// for rows past the end of the sequence.
+constexpr uint32_t kBufferWord3 = 0x00020000u;   // raw 32-bit data format
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, (int)kBufferWord3);
+}
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -125,82 +165,63 @@ __device__ __forceinline__ float half_swap_max(float x) {
     return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-// K/V copies (global -> registers -> LDS) by one wave group; gt is the
-// thread's index in its group.  Rows past N are clamped to row N-1: such
-// keys are masked, and V must stay finite under a zero weight.  The loads are
-// branch-free and every call issues the same number of them, so that the
-// wait before an LDS store counts only the loads issued before its own.
-template <int D>
-using Stage = u32x4[Tile<D>::STAGE];
+// K/V copies.  Rows past the end of the sequence read as zeros (buffer
+// range check): such keys are masked, and a zero V row is finite under a
+// zero weight.  The loads complete asynchronously; the issuing wave waits
+// for them (vmcnt) before the barrier that publishes the tile.  (idx, the
+// wave's index in its group, is uniform over the wave; readfirstlane makes
+// that visible, so the LDS address and the scalar offset need no per-lane
+// handling.  The wave roles themselves stay per-lane values: as wave-uniform
+// values they turn the role branches into scalar branches, and the register
+// allocation of the two roles' code then spills.)
 
+// K tile with first key key0 into `buf`: wave idx of the K group loads chunk
+// columns idx * K_DMA .. +K_DMA-1, lane L fetching key key0 + L.
 template <int D>
-__device__ __forceinline__ void load_k(const u32x4* __restrict__ g, int key0, int N, int gt, Stage<D>& r) {
+__device__ __forceinline__ void dma_k(__amdgpu_buffer_rsrc_t rk, LDS char* buf, int key0, int idx, int lane) {
     using T = Tile<D>;
-    const u32x4* gtile = g + (size_t)key0 * T::ROW_CHUNKS;
-    const int last = N - 1 - key0;             // last valid row of the tile
+    const int widx = __builtin_amdgcn_readfirstlane(idx);
 #pragma unroll
-    for (int c = 0; c < T::K_CHUNKS; ++c) {
-        const int u = c * kGroupThreads + gt;
-        r[c] = gtile[min(u / T::ROW_CHUNKS, last) * T::ROW_CHUNKS + u % T::ROW_CHUNKS];
+    for (int i = 0; i < T::K_DMA; ++i) {
+        const int c = widx * T::K_DMA + i;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (LDS void*)(buf + c * (T::BC * 16)), 16, lane * (2 * D),
+                                                 key0 * (2 * D) + 16 * c, 0, 0);
     }
 }
 
+// V tile with first key key0 into `buf`: wave idx of the V group issues
+// loads n = idx * V_DMA .. +V_DMA-1; load n fills bytes [1024 n, 1024 n +
+// 1024) of the buffer, i.e. keys V_ROWS n + L / ROW_CHUNKS at chunk position
+// L % ROW_CHUNKS for lane L, which fetches the chunk that the permutation
+// puts there.  (V_ROWS n is a multiple of 4, so vswz sees only L's row.)
 template <int D>
-__device__ __forceinline__ void store_k(LDS char* buf, int gt, const Stage<D>& r) {
+__device__ __forceinline__ void dma_v(__amdgpu_buffer_rsrc_t rv, LDS char* buf, int key0, int idx, int lane) {
     using T = Tile<D>;
+    const int widx = __builtin_amdgcn_readfirstlane(idx);
+    const int r = lane / T::ROW_CHUNKS;
+    const int voff = r * (2 * D) + 16 * ((lane % T::ROW_CHUNKS) ^ vswz<D>(r));
 #pragma unroll
-    for (int c = 0; c < T::K_CHUNKS; ++c) {
-        const int u = c * kGroupThreads + gt;
-        *(LDS u32x4*)(buf + (u / T::ROW_CHUNKS) * T::KPITCH + (u % T::ROW_CHUNKS) * 16) = r[c];
-    }
-}
-
-// V items: u = c * kGroupThreads + gt is (key pair j = u % 32, d chunk
-// c8 = u / 32): rows 2j and 2j+1 of that chunk, into r[2c] and r[2c+1].
-template <int D>
-__device__ __forceinline__ void load_v(const u32x4* __restrict__ g, int key0, int N, int gt, Stage<D>& r) {
-    using T = Tile<D>;
-    const u32x4* gtile = g + (size_t)key0 * T::ROW_CHUNKS;
-    const int last = N - 1 - key0;
-#pragma unroll
-    for (int c = 0; c < T::V_ITEMS; ++c) {
-        const int u = c * kGroupThreads + gt;
-        const int j = u & 31, c8 = u >> 5;
-        r[2 * c] = gtile[min(2 * j, last) * T::ROW_CHUNKS + c8];
-        r[2 * c + 1] = gtile[min(2 * j + 1, last) * T::ROW_CHUNKS + c8];
-    }
-}
-
-// Permuted position of key k (0..BC-1) inside a V^T row: within each 16-key
-// chunk, key 8*b3 + 4*b2 + b moves to 8*b2 + 4*b3 + b.
-__device__ __forceinline__ int vt_pos(int k) {
-    return (k & ~15) | ((k & 4) << 1) | ((k & 8) >> 1) | (k & 3);
-}
-
-template <int D>
-__device__ __forceinline__ void store_vt(LDS char* buf, int gt, const Stage<D>& r) {
-    using T = Tile<D>;
-#pragma unroll
-    for (int c = 0; c < T::V_ITEMS; ++c) {
-        const int u = c * kGroupThreads + gt;
-        const int j = u & 31, c8 = u >> 5;
-        LDS char* dst = buf + 8 * c8 * T::VPITCH + vt_pos(2 * j) * 2;   // keys 2j, 2j+1 stay adjacent
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            // d = 8*c8 + 2e and 2e+1: pack (V[2j][d], V[2j+1][d]) for each d
-            const uint32_t a = __builtin_amdgcn_perm(r[2 * c + 1][e], r[2 * c][e], 0x05040100u);
-            const uint32_t b = __builtin_amdgcn_perm(r[2 * c + 1][e], r[2 * c][e], 0x07060302u);
-            *(LDS uint32_t*)(dst + (2 * e) * T::VPITCH) = a;
-            *(LDS uint32_t*)(dst + (2 * e + 1) * T::VPITCH) = b;
-        }
+    for (int i = 0; i < T::V_DMA; ++i) {
+        const int n = widx * T::V_DMA + i;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (LDS void*)(buf + 1024 * n), 16, voff,
+                                                 key0 * (2 * D) + 1024 * n, 0, 0);
     }
 }
 
 // The matrix phase of one tile step: O^T += V^T P^T for the previous tile
-// (HAS_PV) and S^T = K Q^T for the current one (HAS_S), as one stream of
-// 16-byte LDS operand reads and MFMAs.  The reads run kAhead MFMAs ahead of
-// their use (scheduling groups below), so the LDS latency stays hidden
-// behind the matrix core instead of stalling every MFMA.
+// (HAS_PV) and S^T = K Q^T for the current one (HAS_S), as one stream of LDS
+// operand reads and MFMAs.  The reads run kAhead MFMAs ahead of their use
+// (scheduling groups below), so the LDS latency stays hidden behind the
+// matrix core instead of stalling every MFMA.
+//
+// The V^T operand of the P V product (32 d x 16 keys, keys in the order of
+// P's registers: lane l holds d = 32 db + l % 32 and keys 16 cc + 4h + 0..3,
+// then 16 cc + 8 + 4h + 0..3) comes from two transposing reads.  In a
+// transposing read, lane i of each 16-lane group receives element i % 4 of
+// the 4-element pieces addressed by lanes i / 4, i / 4 + 4, i / 4 + 8 and
+// i / 4 + 12 of its group.  So lane j of group g addresses key
+// 16 cc + 8q + 4h + j / 4 at d = 32 db + 16 (g % 2) + 4 (j % 4), and read q
+// returns to each lane its 4 keys of run q for its d.
 constexpr int kAhead = 4;
 
 template <bool B>
@@ -222,17 +243,22 @@ __device__ __forceinline__ void gemm_phase(const LDS char* vl, const LDS char* k
     constexpr int NF = NPV + NS;
     const int h = lane >> 5;
     const int l32 = lane & 31;
-    const LDS char* vrow = vl + l32 * T::VPITCH + 16 * h;
-    const LDS char* krow = kl + l32 * T::KPITCH + 16 * h;
+    const LDS char* krow = kl + (h * T::BC + l32) * 16;     // chunk h, key l32
+    const int vr = 4 * h + ((lane & 15) >> 2);               // key of this lane's piece, within the run
+    const int dlo = 16 * ((lane >> 4) & 1) + 4 * (lane & 3); // d of its piece, within the 32-d block
     bf16x8 fr[NF > 0 ? NF : 1];
 #pragma unroll
     for (int i = 0; i < NF; ++i) {
         if (i < NPV) {
             const int cc = i / DB, db = i % DB;
-            fr[i] = *(const LDS bf16x8*)(vrow + 32 * db * T::VPITCH + 32 * cc);
+            const LDS char* vp = vl + (16 * cc + vr) * (2 * D) + 16 * ((4 * db + dlo / 8) ^ vswz<D>(vr)) +
+                                 2 * (dlo % 8);
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS i16x4*)vp);
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS i16x4*)(vp + 8 * (2 * D)));
+            fr[i] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         } else {
             const int ks = (i - NPV) / T::KB, kb = (i - NPV) % T::KB;
-            fr[i] = *(const LDS bf16x8*)(krow + 32 * kb * T::KPITCH + 32 * ks);
+            fr[i] = *(const LDS bf16x8*)(krow + (2 * ks * T::BC + 32 * kb) * 16);
         }
     }
     if constexpr (HAS_S) {
@@ -249,12 +275,17 @@ __device__ __forceinline__ void gemm_phase(const LDS char* vl, const LDS char* k
             s[kb] = mfma32(fr[i], qf[ks], s[kb]);
         }
     }
+    // A P V operand takes two reads, an S operand one.
     if constexpr (NF > kAhead) {
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kAhead, 0);
+        constexpr int first_reads = NPV >= kAhead ? 2 * kAhead : 2 * NPV + (kAhead - NPV);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, first_reads, 0);
 #pragma unroll
         for (int i = 0; i < NF - kAhead; ++i) {
             __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+            if (i + kAhead < NPV)
+                __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+            else
+                __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
         }
         __builtin_amdgcn_sched_group_barrier(kSchedMfma, kAhead, 0);
     }
@@ -476,9 +507,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     const int w_kv_end = CAUSAL ? min(N, wq0 + kWaveRows) : N;
     const int w_tiles = (wq0 < N) ? max(0, min(kt_hi, (w_kv_end + BC - 1) / BC) - kt_lo) : 0;
 
-    const u32x4* kg = (const u32x4*)(K + kv_head + (size_t)kt_lo * BC * D);
-    const u32x4* vg = (const u32x4*)(V + kv_head + (size_t)kt_lo * BC * D);
     const int Nl = N - kt_lo * BC;           // keys from the first tile of the range on
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + kv_head + (size_t)kt_lo * BC * D, (uint32_t)Nl * (2 * D));
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + kv_head + (size_t)kt_lo * BC * D, (uint32_t)Nl * (2 * D));
 
     f32x16 oacc[DB];
 #pragma unroll
@@ -488,20 +519,20 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     f32x16 s[KB];
     bf16x8 pb[BC / 16];
 
-    // K/V copies.  The second group copies the K tiles, the first group the
-    // V tiles, and only a group in its vector phase writes to LDS, so the
-    // matrix phases carry no copy work beyond issuing loads.  Each wave has
-    // one staging set: a group loads a tile at the start of its matrix phase
-    // and writes it to LDS at the end of its next vector phase; tile i lives
-    // in LDS buffer i&1.
-    //   K_{u+1} is loaded in phase 2u-1 and written at the end of phase 2u,
-    //   over K_{u-1}, whose last reader (second group, matrix phase u-1) ran
-    //   in phase 2u-1; it is first read in phase 2u+2.
-    //   V_u is loaded in phase 2u and written at the end of phase 2u+1, over
-    //   V_{u-2}, last read in phase 2u-1; it is first read in phase 2u+2.
-    // Past the last tile the loads repeat the last tile (in bounds, never
-    // stored), so every copy issues the same loads.
-    const int gt = idx * 64 + lane;            // thread index within the group
+    // K/V copies, by direct loads issued at the end of a matrix phase (after
+    //   the phase's LDS reads: the compiler makes a transposing LDS read wait
+    //   for every direct load the wave may still have in flight, so a load
+    //   issued before them would stall the phase).  Each load then has the
+    //   issuing group's vector phase to land; the group waits for it before
+    //   that phase's closing barrier.
+    //   K: tile t lives in K buffer t % 3.  The second group loads K_{u+2} at
+    //   the end of its matrix phase u (phase 2u+1), over K_{u-1}, whose
+    //   readers ran in phases 2u-2 and 2u-1.  (With two buffers the target
+    //   would still hold K_u, which the other waves of the group may still be
+    //   reading in that same phase.)  K_{u+2} is first read in phase 2u+4.
+    //   V: tile t lives in V buffer t & 1.  The first group loads V_u at the
+    //   end of its matrix phase u (phase 2u), over V_{u-2}, whose readers ran
+    //   in phases 2u-2 and 2u-1; V_u is first read in phase 2u+2.
     if (SPLIT && n_tiles == 0) {               // no key of the range is visible to the tile
         if (my_row < N && wq0 < N) {
             const size_t prow = ((size_t)split * bh_total + bh) * N + my_row;
@@ -515,11 +546,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
         }
         return;
     }
-    Stage<D> stg;
     if (grp == 1) {
-        load_k<D>(kg, 0, Nl, gt, stg);
-        store_k<D>(smem + T::K0, gt, stg);
-        load_k<D>(kg, min(1, n_tiles - 1) * BC, Nl, gt, stg);
+        dma_k<D>(rk, smem, 0, idx, lane);
+        if (n_tiles > 1) dma_k<D>(rk, smem + T::KBYTES, BC, idx, lane);
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);
     }
     __syncthreads();
 
@@ -531,7 +561,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
         const bool has_pv = t >= 1 && t - 1 < w_tiles;
         const bool has_s = t < w_tiles;
         const LDS char* vl = smem + ((t - 1) & 1 ? T::V1 : T::V0);
-        const LDS char* kl = smem + (t & 1 ? T::K1 : T::K0);
+        const LDS char* kl = smem + (t % T::NKBUF) * T::KBYTES;
         // The wave on the same SIMD runs vector work meanwhile; a higher
         // issue priority keeps the MFMAs from waiting behind it.
         __builtin_amdgcn_s_setprio(kMatrixPrio);
@@ -558,21 +588,21 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     // Phases 2u and 2u+1.
     auto tile_pair = [&](auto masked, int u) __attribute__((always_inline)) {
         if (grp == 0) {
-            load_v<D>(vg, min(u, n_tiles - 1) * BC, Nl, gt, stg);
             matrix_phase(u);
+            if (u < n_tiles) dma_v<D>(rv, smem + (u & 1 ? T::V1 : T::V0), u * BC, idx, lane);
         } else {            // vector phase of tile u-1 of the second group
             softmax_phase(masked, u - 1);
-            if (u + 1 < n_tiles) store_k<D>(smem + ((u + 1) & 1 ? T::K1 : T::K0), gt, stg);
+            __builtin_amdgcn_s_waitcnt(kWaitVm0);       // K_{u+1} has landed
         }
-        __syncthreads();
+        lds_barrier();
         if (grp == 0) {     // vector phase of tile u of the first group
             softmax_phase(masked, u);
-            if (u < n_tiles) store_vt<D>(smem + (u & 1 ? T::V1 : T::V0), gt, stg);
+            __builtin_amdgcn_s_waitcnt(kWaitVm0);       // V_u has landed
         } else {
-            load_k<D>(kg, min(u + 2, n_tiles - 1) * BC, Nl, gt, stg);
             matrix_phase(u);
+            if (u + 2 < n_tiles) dma_k<D>(rk, smem + ((u + 2) % T::NKBUF) * T::KBYTES, (u + 2) * BC, idx, lane);
         }
-        __syncthreads();
+        lds_barrier();
     };
     // Local tile t holds keys from (kt_lo + t) BC on.  No key of a tile
     // before t_mask is dead for any row of the workgroup: the tail starts at

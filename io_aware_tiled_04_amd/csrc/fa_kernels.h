@@ -69,6 +69,9 @@ hipError_t launch_bwd_bf16_dropout(const BwdArgs& a, const Dropout& dr, float* w
 constexpr int kBlockRowsBf16 = 256;
 // Query rows per workgroup of the fp32 kernel.
 constexpr int kBlockRowsF32 = 64;
+// Longest sequence: the bf16 forward addresses one head's K or V (N * d * 2
+// bytes) through buffer descriptors with 32-bit byte offsets.
+constexpr int kMaxSeqLen = 1 << 23;
 // Resident rows per workgroup of the backward kernels.
 constexpr int kBwdBlockRows = 128;
 // Keys per tile of the bf16 kernel (the granularity of split-KV ranges).

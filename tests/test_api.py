@@ -60,6 +60,7 @@ P = 0x1000
     ((P, P, P, P, P, 1, 1, 1, 0, 64, 0, 0.125), "FA_ERR_SHAPE"),
     ((P, P, P, P, P, 1, 1, 1, -5, 64, 0, 0.125), "FA_ERR_SHAPE"),
     ((P, P, P, P, P, 65536, 65536, 1, 4096, 64, 0, 0.125), "FA_ERR_SHAPE"),
+    ((P, P, P, P, P, 1, 1, 1, (1 << 23) + 1, 64, 0, 0.125), "FA_ERR_SHAPE"),
     ((P, P, P, P, P, 1, 6, 4, 128, 64, 1, 0.125), "FA_ERR_HEADS"),
     ((P, P, P, P, P, 1, 1, 1, 128, 96, 1, 0.125), "FA_ERR_HEADDIM"),
     ((P, P, P, P, P, 1, 1, 1, 128, 256, 1, 0.125), "FA_ERR_HEADDIM"),
