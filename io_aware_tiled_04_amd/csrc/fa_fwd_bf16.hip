@@ -99,7 +99,7 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
 }
 
-// K/V tile geometry in LDS: three K buffers and two V buffers, all filled
+// K/V tile geometry in LDS: two K buffers and two V buffers, all filled
 // by direct global-to-LDS loads (one wave instruction writes 1 KiB: 16 bytes
 // per lane, in lane order).
 //  * K is stored chunk-major: the 16-byte chunk c (d = 8c .. 8c+7) of key r
@@ -118,9 +118,9 @@ struct Tile {
     static constexpr int ROW_CHUNKS = D / 8;      // 16-byte chunks per row
     static constexpr int KBYTES = BC * D * 2;
     static constexpr int VBYTES = BC * D * 2;
-    static constexpr int NKBUF = 3;               // K ring: tile t in buffer t % 3
-    static constexpr int V0 = NKBUF * KBYTES, V1 = V0 + VBYTES;
-    static constexpr int ROLE = V1 + VBYTES;      // 16 ints for the wave roles
+    static constexpr int NBUF = 2;                // K and V rings: tile t in buffer t % 2
+    static constexpr int VBASE = NBUF * KBYTES;
+    static constexpr int ROLE = VBASE + NBUF * VBYTES;   // 16 ints for the wave roles
     static constexpr int LDS_BYTES = ROLE + 64;
     // Direct loads per wave: the K group's 4 waves load a K tile (ROW_CHUNKS
     // loads), the V group's 4 waves a V tile (VBYTES / 1024 loads of V_ROWS
@@ -144,10 +144,32 @@ __device__ __forceinline__ int vswz(int r) {
 
 // Buffer descriptor of a raw byte range: loads at or past `bytes` return
 // zeros (the descriptor's range check), which is what the tile copies use
-// for rows past the end of the sequence.
-constexpr uint32_t kBufferWord3 = 0x00020000u;   // raw 32-bit data format
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, (int)kBufferWord3);
+// for rows past the end of the sequence.  Words: base address (48 bits,
+// stride 0), number of bytes, raw 32-bit data format.
+constexpr uint32_t kBufferWord3 = 0x00020000u;
+__device__ __forceinline__ u32x4 make_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t a = (uint64_t)(uintptr_t)base;
+    u32x4 r;
+    r[0] = (uint32_t)a;
+    r[1] = (uint32_t)(a >> 32) & 0xFFFFu;
+    r[2] = bytes;
+    r[3] = kBufferWord3;
+    return r;
+}
+
+// One direct global-to-LDS load: lane L's 16 bytes at (descriptor base +
+// voff + soff) go to LDS address dst + 16 L.  Written as inline assembly
+// on purpose: the compiler does not see it as a write to LDS, so it does not
+// make the transposing LDS reads of other buffers wait for it (it cannot
+// tell the ring buffers apart).  Completion is the caller's business: a
+// vmcnt wait before the barrier that publishes the tile.  M0 holds the LDS
+// address; nothing else in the kernel uses M0.
+__device__ __forceinline__ void dma16(LDS char* dst, u32x4 rsrc, uint32_t voff, uint32_t soff) {
+    const uint32_t m = (uint32_t)(uintptr_t)dst;
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :
+                 : "s"(m), "v"(voff), "s"(rsrc), "s"(soff)
+                 : "memory", "m0");
 }
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -178,14 +200,13 @@ __device__ __forceinline__ float half_swap_max(float x) {
 // K tile with first key key0 into `buf`: wave idx of the K group loads chunk
 // columns idx * K_DMA .. +K_DMA-1, lane L fetching key key0 + L.
 template <int D>
-__device__ __forceinline__ void dma_k(__amdgpu_buffer_rsrc_t rk, LDS char* buf, int key0, int idx, int lane) {
+__device__ __forceinline__ void dma_k(u32x4 rk, LDS char* buf, int key0, int idx, int lane) {
     using T = Tile<D>;
     const int widx = __builtin_amdgcn_readfirstlane(idx);
 #pragma unroll
     for (int i = 0; i < T::K_DMA; ++i) {
         const int c = widx * T::K_DMA + i;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (LDS void*)(buf + c * (T::BC * 16)), 16, lane * (2 * D),
-                                                 key0 * (2 * D) + 16 * c, 0, 0);
+        dma16(buf + c * (T::BC * 16), rk, lane * (2 * D), key0 * (2 * D) + 16 * c);
     }
 }
 
@@ -195,7 +216,7 @@ __device__ __forceinline__ void dma_k(__amdgpu_buffer_rsrc_t rk, LDS char* buf, 
 // L % ROW_CHUNKS for lane L, which fetches the chunk that the permutation
 // puts there.  (V_ROWS n is a multiple of 4, so vswz sees only L's row.)
 template <int D>
-__device__ __forceinline__ void dma_v(__amdgpu_buffer_rsrc_t rv, LDS char* buf, int key0, int idx, int lane) {
+__device__ __forceinline__ void dma_v(u32x4 rv, LDS char* buf, int key0, int idx, int lane) {
     using T = Tile<D>;
     const int widx = __builtin_amdgcn_readfirstlane(idx);
     const int r = lane / T::ROW_CHUNKS;
@@ -203,8 +224,7 @@ __device__ __forceinline__ void dma_v(__amdgpu_buffer_rsrc_t rv, LDS char* buf, 
 #pragma unroll
     for (int i = 0; i < T::V_DMA; ++i) {
         const int n = widx * T::V_DMA + i;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (LDS void*)(buf + 1024 * n), 16, voff,
-                                                 key0 * (2 * D) + 1024 * n, 0, 0);
+        dma16(buf + 1024 * n, rv, voff, key0 * (2 * D) + 1024 * n);
     }
 }
 
@@ -508,8 +528,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     const int w_tiles = (wq0 < N) ? max(0, min(kt_hi, (w_kv_end + BC - 1) / BC) - kt_lo) : 0;
 
     const int Nl = N - kt_lo * BC;           // keys from the first tile of the range on
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + kv_head + (size_t)kt_lo * BC * D, (uint32_t)Nl * (2 * D));
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + kv_head + (size_t)kt_lo * BC * D, (uint32_t)Nl * (2 * D));
+    const u32x4 rk = make_rsrc(K + kv_head + (size_t)kt_lo * BC * D, (uint32_t)Nl * (2 * D));
+    const u32x4 rv = make_rsrc(V + kv_head + (size_t)kt_lo * BC * D, (uint32_t)Nl * (2 * D));
 
     f32x16 oacc[DB];
 #pragma unroll
@@ -519,20 +539,18 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     f32x16 s[KB];
     bf16x8 pb[BC / 16];
 
-    // K/V copies, by direct loads issued at the end of a matrix phase (after
-    //   the phase's LDS reads: the compiler makes a transposing LDS read wait
-    //   for every direct load the wave may still have in flight, so a load
-    //   issued before them would stall the phase).  Each load then has the
-    //   issuing group's vector phase to land; the group waits for it before
-    //   that phase's closing barrier.
-    //   K: tile t lives in K buffer t % 3.  The second group loads K_{u+2} at
-    //   the end of its matrix phase u (phase 2u+1), over K_{u-1}, whose
-    //   readers ran in phases 2u-2 and 2u-1.  (With two buffers the target
-    //   would still hold K_u, which the other waves of the group may still be
-    //   reading in that same phase.)  K_{u+2} is first read in phase 2u+4.
-    //   V: tile t lives in V buffer t & 1.  The first group loads V_u at the
-    //   end of its matrix phase u (phase 2u), over V_{u-2}, whose readers ran
-    //   in phases 2u-2 and 2u-1; V_u is first read in phase 2u+2.
+    // K/V copies: direct loads, each wave of a group loading its share; tile
+    // t of K and of V lives in ring buffer t & 1.  Each load is issued right
+    // after a barrier that retired the previous readers of its buffer, and
+    // has two phases to land before the barrier that publishes it.
+    //   K (second group): K_0 before the loop.  At the start of its vector
+    //   phase 2u the group issues K_{u+1}, over K_{u-1} (read in phases 2u-2
+    //   and 2u-1), and waits for it at the end of its matrix phase 2u+1; it
+    //   is first read in phase 2u+2.
+    //   V (first group): at the start of its matrix phase 2u the group issues
+    //   V_u, over V_{u-2} (read in phases 2u-2 and 2u-1), while that phase
+    //   reads V_{u-1} from the other buffer, and waits for it at the end of
+    //   its vector phase 2u+1; it is first read in phase 2u+2.
     if (SPLIT && n_tiles == 0) {               // no key of the range is visible to the tile
         if (my_row < N && wq0 < N) {
             const size_t prow = ((size_t)split * bh_total + bh) * N + my_row;
@@ -548,7 +566,6 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     }
     if (grp == 1) {
         dma_k<D>(rk, smem, 0, idx, lane);
-        if (n_tiles > 1) dma_k<D>(rk, smem + T::KBYTES, BC, idx, lane);
         __builtin_amdgcn_s_waitcnt(kWaitVm0);
     }
     __syncthreads();
@@ -560,8 +577,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     auto matrix_phase = [&](int t) __attribute__((always_inline)) {
         const bool has_pv = t >= 1 && t - 1 < w_tiles;
         const bool has_s = t < w_tiles;
-        const LDS char* vl = smem + ((t - 1) & 1 ? T::V1 : T::V0);
-        const LDS char* kl = smem + (t % T::NKBUF) * T::KBYTES;
+        const LDS char* vl = smem + T::VBASE + ((t - 1) & 1) * T::VBYTES;
+        const LDS char* kl = smem + (t & 1) * T::KBYTES;
         // The wave on the same SIMD runs vector work meanwhile; a higher
         // issue priority keeps the MFMAs from waiting behind it.
         __builtin_amdgcn_s_setprio(kMatrixPrio);
@@ -588,19 +605,19 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     // Phases 2u and 2u+1.
     auto tile_pair = [&](auto masked, int u) __attribute__((always_inline)) {
         if (grp == 0) {
+            if (u < n_tiles) dma_v<D>(rv, smem + T::VBASE + (u & 1) * T::VBYTES, u * BC, idx, lane);
             matrix_phase(u);
-            if (u < n_tiles) dma_v<D>(rv, smem + (u & 1 ? T::V1 : T::V0), u * BC, idx, lane);
         } else {            // vector phase of tile u-1 of the second group
+            if (u + 1 < n_tiles) dma_k<D>(rk, smem + ((u + 1) & 1) * T::KBYTES, (u + 1) * BC, idx, lane);
             softmax_phase(masked, u - 1);
-            __builtin_amdgcn_s_waitcnt(kWaitVm0);       // K_{u+1} has landed
         }
         lds_barrier();
         if (grp == 0) {     // vector phase of tile u of the first group
             softmax_phase(masked, u);
-            __builtin_amdgcn_s_waitcnt(kWaitVm0);       // V_u has landed
+            __builtin_amdgcn_s_waitcnt(kWaitVm0);    // V_u has landed
         } else {
             matrix_phase(u);
-            if (u + 2 < n_tiles) dma_k<D>(rk, smem + ((u + 2) % T::NKBUF) * T::KBYTES, (u + 2) * BC, idx, lane);
+            __builtin_amdgcn_s_waitcnt(kWaitVm0);    // K_{u+1} has landed
         }
         lds_barrier();
     };
