@@ -637,8 +637,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
 
     if (wq0 >= N) return;
     const float l_tot = half_swap_sum(l_run);
-    if (my_row >= N) return;
     if constexpr (SPLIT) {
+        if (my_row >= N) return;
         const bool seen = l_tot > 0.f;       // the row saw some key of the range
         const float inv = seen ? 1.f / l_tot : 0.f;
         const size_t prow = ((size_t)split * bh_total + bh) * N + my_row;
@@ -654,8 +654,22 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
             LP[prow] = seen ? (m_run + __builtin_log2f(l_tot)) * 0.69314718055994531f : -__builtin_inff();
         return;
     }
+    // O through LDS.  In registers a lane holds 4-element runs of its row,
+    // so direct stores would write 16-byte pieces of 32 rows per instruction.
+    // The wave writes its 32 x D tile (bf16) into its own slice of the idle
+    // K/V rings, with the 16-byte chunk c of row r at position c ^ (r mod RC),
+    // then reads back whole rows and stores 1 KiB of consecutive rows per
+    // instruction.  (Every LDS read of the rings ended at the loop's last
+    // barrier, and no copy is in flight.)
+    constexpr int RC = D / 8;                        // 16-byte chunks per row
+    constexpr int RPI = 1024 / (2 * D);              // rows per store instruction
+    static_assert(kWaves * kWaveRows * 2 * D <= T::VBASE + T::NBUF * T::VBYTES, "O staging fits the rings");
     const float inv = DROP ? dr.factor / l_tot : 1.f / l_tot;
-    __bf16* op = O + q_head + (size_t)my_row * D;
+    LDS char* ot = smem + wave * (kWaveRows * 2 * D);
+    // (the per-lane swizzle keys are hidden from the optimiser, which would
+    // otherwise precompute all 24 addresses and keep them live from the start)
+    int wsw = l32 % RC, rsw = (lane / RC) % RC;
+    asm volatile("" : "+v"(wsw), "+v"(rsw));
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
 #pragma unroll
@@ -663,10 +677,18 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
             bf16x4 out;
 #pragma unroll
             for (int r = 0; r < 4; ++r) out[r] = (__bf16)(oacc[db][4 * g + r] * inv);
-            *(bf16x4*)(op + 32 * db + 8 * g + 4 * h) = out;
+            *(LDS bf16x4*)(ot + l32 * (2 * D) + 16 * ((4 * db + g) ^ wsw) + 8 * h) = out;
         }
     }
-    if (h == 0) LSE[(size_t)bh * N + my_row] = (m_run + __builtin_log2f(l_tot)) * 0.69314718055994531f;
+    __bf16* otile = O + q_head + (size_t)wq0 * D;
+#pragma unroll
+    for (int i = 0; i < kWaveRows / RPI; ++i) {
+        // row r = i RPI + lane / RC, and r mod RC = (i RPI + rsw) mod RC
+        const int r = i * RPI + lane / RC, c = lane % RC;
+        const u32x4 x = *(const LDS u32x4*)(ot + r * (2 * D) + 16 * (c ^ ((i * RPI + rsw) % RC)));
+        if (wq0 + r < N) *(u32x4*)(otile + (size_t)r * D + 8 * c) = x;
+    }
+    if (h == 0 && my_row < N) LSE[(size_t)bh * N + my_row] = (m_run + __builtin_log2f(l_tot)) * 0.69314718055994531f;
 }
 
 template <int D, bool CAUSAL, bool SPLIT, bool DROP = false>
