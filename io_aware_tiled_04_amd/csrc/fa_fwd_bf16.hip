@@ -130,6 +130,7 @@ struct Tile {
     static constexpr int V_DMA = VBYTES / 1024 / 4;
     static_assert(BC == 64, "a direct K load covers one chunk of 64 keys");
     static_assert(ROW_CHUNKS % 4 == 0 && (VBYTES / 1024) % 4 == 0, "tiles must split evenly over a wave group");
+    static_assert(ROW_CHUNKS % kWaves == 0, "the first K tile splits evenly over all waves");
 };
 
 // Chunk permutation of V row r (in 16-byte chunks).  The transposing read of
@@ -476,6 +477,27 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
         if (CAUSAL) qt = n_qtiles - 1 - qt;
     }
 
+    // The first K tile does not depend on the wave roles: all 8 waves start
+    // loading it now, so that its latency overlaps the role set-up and the Q
+    // loads.  (Not when the split range holds no visible tile: the
+    // workgroup returns early and must leave no load in flight.)
+    const size_t kv_head = (size_t)(bh / group) * N * D;
+    const int kt_lo = split * kq + min(split, kr);
+    const int kt_hi = kt_lo + kq + (split < kr ? 1 : 0);
+    const int kv_end = CAUSAL ? min(N, qt * kBr + kBr) : N;  // keys this workgroup needs
+    const int n_tiles = max(0, min(kt_hi, (kv_end + BC - 1) / BC) - kt_lo);
+    const int Nl = N - kt_lo * BC;           // keys from the first tile of the range on
+    const u32x4 rk = make_rsrc(K + kv_head + (size_t)kt_lo * BC * D, (uint32_t)Nl * (2 * D));
+    const u32x4 rv = make_rsrc(V + kv_head + (size_t)kt_lo * BC * D, (uint32_t)Nl * (2 * D));
+    if (n_tiles > 0) {
+        const int w0 = __builtin_amdgcn_readfirstlane(wave);
+#pragma unroll
+        for (int i = 0; i < T::ROW_CHUNKS / kWaves; ++i) {
+            const int c = w0 * (T::ROW_CHUNKS / kWaves) + i;
+            dma16(smem + c * (T::BC * 16), rk, lane * (2 * D), 16 * c);
+        }
+    }
+
     // Wave roles.  Order the waves by (rank among the waves on the same SIMD,
     // SIMD id, wave id): the first four form the group that starts with a
     // matrix phase, the last four the group that starts one phase later, so
@@ -501,7 +523,6 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     const int rblock = 2 * idx + grp;         // the groups interleave 32-row blocks
 
     const size_t q_head = (size_t)bh * N * D;
-    const size_t kv_head = (size_t)(bh / group) * N * D;
     const int q0 = qt * kBr;
     const int wq0 = q0 + rblock * kWaveRows;  // first query row of this wave
     const int my_row = wq0 + l32;             // the query row this lane owns
@@ -520,16 +541,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     }
 
     // Key tiles: local tile t is global tile kt_lo + t (kt_lo = 0 unless SPLIT).
-    const int kt_lo = split * kq + min(split, kr);
-    const int kt_hi = kt_lo + kq + (split < kr ? 1 : 0);
-    const int kv_end = CAUSAL ? min(N, q0 + kBr) : N;       // keys this workgroup needs
-    const int n_tiles = max(0, min(kt_hi, (kv_end + BC - 1) / BC) - kt_lo);
     const int w_kv_end = CAUSAL ? min(N, wq0 + kWaveRows) : N;
     const int w_tiles = (wq0 < N) ? max(0, min(kt_hi, (w_kv_end + BC - 1) / BC) - kt_lo) : 0;
-
-    const int Nl = N - kt_lo * BC;           // keys from the first tile of the range on
-    const u32x4 rk = make_rsrc(K + kv_head + (size_t)kt_lo * BC * D, (uint32_t)Nl * (2 * D));
-    const u32x4 rv = make_rsrc(V + kv_head + (size_t)kt_lo * BC * D, (uint32_t)Nl * (2 * D));
 
     f32x16 oacc[DB];
 #pragma unroll
@@ -543,7 +556,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     // t of K and of V lives in ring buffer t & 1.  Each load is issued right
     // after a barrier that retired the previous readers of its buffer, and
     // has two phases to land before the barrier that publishes it.
-    //   K (second group): K_0 before the loop.  At the start of its vector
+    //   K (second group; K_0 by all waves before the loop).  At the start of its vector
     //   phase 2u the group issues K_{u+1}, over K_{u-1} (read in phases 2u-2
     //   and 2u-1), and waits for it at the end of its matrix phase 2u+1; it
     //   is first read in phase 2u+2.
@@ -564,10 +577,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
         }
         return;
     }
-    if (grp == 1) {
-        dma_k<D>(rk, smem, 0, idx, lane);
-        __builtin_amdgcn_s_waitcnt(kWaitVm0);
-    }
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);      // this wave's share of K_0 (and its Q rows)
     __syncthreads();
 
     // Phases p = 0 .. 2*n_tiles+1, each closed by a workgroup barrier.  The
