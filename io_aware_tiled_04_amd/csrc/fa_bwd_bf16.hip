@@ -140,15 +140,23 @@ __device__ __forceinline__ void put_transposed(LDS char* dst, int tid, const u32
     }
 }
 
-// Row statistics of the streamed query rows (DK, DV): LSE * log2(e) and D.
-// Rows past N get +inf (so that p = 0) and D = 0.
+// Row statistics of the streamed query rows (dK/dV kernel): LSE * log2(e)
+// and D.  Staged raw, one step ahead like the tiles, and finished when
+// stored: any arithmetic on the loaded values at load time would make the
+// wave wait right there for every load it has in flight, the tile loads
+// issued just before included.  Rows past N get +inf (so that p = 0) and
+// D = 0.
 __device__ __forceinline__ void stage_stats(const float* __restrict__ lse, const float* __restrict__ dd,
-                                            int row0, int n, int tid, float& s0, float& s1) {
-    const int r = row0 + (tid & 31);
-    const bool in = r < n;
-    const int rc = min(r, n - 1);
-    s0 = in ? lse[rc] * kLog2e : __builtin_inff();
-    s1 = in && dd ? dd[rc] : 0.f;
+                                            int row0, int n, int tid, float& s0, float& s1, int& srow) {
+    srow = row0 + (tid & 31);
+    const int rc = min(srow, n - 1);
+    s0 = lse[rc];
+    s1 = dd[rc];
+}
+__device__ __forceinline__ void finish_stats(float s0, float s1, int srow, int n, float& lse2, float& dv) {
+    const bool in = srow < n;
+    lse2 = in ? s0 * kLog2e : __builtin_inff();
+    dv = in ? s1 : 0.f;
 }
 
 // D_i = sum_d dO_id O_id for every row: D / 8 threads per row, one 16-byte
@@ -260,11 +268,16 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
         put_transposed<D>(base + L::T, tid, stg.x0, stg.x1);
     };
 
-    if (n_steps > 0) {
-        load_step(0);
-        store_step(0);
-        load_step(1);
-    }
+    // n_steps >= 1: the workgroup's first row is below N, so key tile 0 is
+    // always visible.
+    load_step(0);
+    store_step(0);
+    // The row statistics arrived with (before) the first tile.  Redefining
+    // them here tells the compiler so; otherwise it cannot prove it on every
+    // path into the loop and waits for all loads in flight at their first
+    // use in every step.
+    asm volatile("" : "+v"(lse2_lane), "+v"(d_lane));
+    load_step(1);
     __syncthreads();
 
 #pragma unroll 1
@@ -457,20 +470,23 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(
     const bool copy_do = tid >= 256;
     u32x4 x0, x1;
     float s0 = 0.f, s1 = 0.f;
+    int srow = 0;
     auto load_step = [&](int step) __attribute__((always_inline)) {
         const int st = min(step, n_steps - 1);
         const int hs = st / per_head;
         const int row0 = (t_begin + st % per_head) * kTile;
         stage_rows<D>((copy_do ? dO : Q) + q_head(hs) * D, row0, N, ct, x0, x1);
-        if (tid < kTile) stage_stats(LSE + q_head(hs), Dd + q_head(hs), row0, N, tid, s0, s1);
+        if (tid < kTile) stage_stats(LSE + q_head(hs), Dd + q_head(hs), row0, N, tid, s0, s1, srow);
     };
     auto store_step = [&](int set) __attribute__((always_inline)) {
         LDS char* base = smem + set * L::SET;
         put_rows<D>(base + (copy_do ? L::B : L::A), ct, x0, x1);
         put_transposed<D>(base + (copy_do ? L::TO : L::TQ), ct, x0, x1);
         if (tid < kTile) {
-            ((LDS float*)(base + L::S))[tid] = s0;
-            ((LDS float*)(base + L::S))[kTile + tid] = s1;
+            float lse2, dv;
+            finish_stats(s0, s1, srow, N, lse2, dv);
+            ((LDS float*)(base + L::S))[tid] = lse2;
+            ((LDS float*)(base + L::S))[kTile + tid] = dv;
         }
     };
 
