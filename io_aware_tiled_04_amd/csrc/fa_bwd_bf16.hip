@@ -67,6 +67,24 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// Instruction order for a run of N MFMAs whose A operands are N LDS reads
+// written before them: the reads go kAhead MFMAs ahead of their use, so that
+// an MFMA does not wait for a read issued just before it.  (Groups for the
+// scheduler: mask 0x100 = LDS reads, 0x008 = MFMAs.)
+constexpr int kAhead = 4;
+template <int N>
+__device__ __forceinline__ void reads_ahead() {
+    if constexpr (N > kAhead) {
+        __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
+#pragma unroll
+        for (int i = 0; i < N - kAhead; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 0);
+    }
+}
+
 // Keep decision of the draw in 16-bit half `hi` of a generator word.
 __device__ __forceinline__ bool keep_half(uint32_t word, int hi, uint32_t t) {
     return (hi ? word >> 16 : word & 0xFFFFu) >= t;
@@ -316,20 +334,37 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
             // score products: S^T and dP^T with one query per lane
             const LDS char* arow = base + L::A + l32 * L::RPITCH + 16 * h;
             const LDS char* brow = base + L::B + l32 * L::RPITCH + 16 * h;
+            bf16x8 fa[2 * KS];
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                fa[2 * ks] = *(const LDS bf16x8*)(arow + 32 * ks);
+                fa[2 * ks + 1] = *(const LDS bf16x8*)(brow + 32 * ks);
+            }
             f32x16 x = (f32x16){}, y = (f32x16){};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                x = mfma32(*(const LDS bf16x8*)(arow + 32 * ks), rf1[ks], x);
-                y = mfma32(*(const LDS bf16x8*)(brow + 32 * ks), rf2[ks], y);
+                x = mfma32(fa[2 * ks], rf1[ks], x);
+                y = mfma32(fa[2 * ks + 1], rf2[ks], y);
             }
+            reads_ahead<2 * KS>();
             // register i holds key row0 + (i/4)*8 + 4h + i%4
+            float arg[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) arg[i] = fmaf(x[i], c, -lse2_lane);
+            // Dead scores get exp2(-inf) = 0: selects under one uniform branch,
+            // not a branch around each exponential.
+            if (masked) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int key = row0 + (i >> 2) * 8 + 4 * h + (i & 3);
+                    const bool dead = (key >= N) | (my_row >= N) | (CAUSAL & (key > my_row));
+                    arg[i] = dead ? -__builtin_inff() : arg[i];
+                }
+            }
             bf16x8 w[2];
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const int key = row0 + (i >> 2) * 8 + 4 * h + (i & 3);
-                bool dead = false;
-                if (masked) dead = key >= N || my_row >= N || (CAUSAL && key > my_row);
-                const float p = dead ? 0.f : __builtin_amdgcn_exp2f(fmaf(x[i], c, -lse2_lane));
+                const float p = __builtin_amdgcn_exp2f(arg[i]);
                 float val;
                 if constexpr (DROP) {
                     const bool kept = keep_half(kw[i >> 3][(i & 7) >> 1], i & 1, dr.t2 & 0xFFFFu);
@@ -341,12 +376,12 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
             }
             // dQ^T (d x queries) += (K^T) (d x keys) dS^T
             const LDS char* trow = base + L::T + l32 * L::TPITCH + 16 * h;
+            bf16x8 ft[2 * DB];
 #pragma unroll
-            for (int db = 0; db < DB; ++db)
+            for (int i = 0; i < 2 * DB; ++i) ft[i] = *(const LDS bf16x8*)(trow + 32 * (i >> 1) * L::TPITCH + 32 * (i & 1));
 #pragma unroll
-                for (int cc = 0; cc < 2; ++cc)
-                    acc[db] = mfma32(*(const LDS bf16x8*)(trow + 32 * db * L::TPITCH + 32 * cc), w[cc],
-                                     acc[db]);
+            for (int i = 0; i < 2 * DB; ++i) acc[i >> 1] = mfma32(ft[i], w[i & 1], acc[i >> 1]);
+            reads_ahead<2 * DB>();
         }
         if (step + 1 < n_steps) store_step(set ^ 1);
         __syncthreads();
@@ -517,9 +552,13 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(
         uint32_t zword = 0;
         if (active) {
             const LDS char* srow = base + (dk_role ? L::A : L::B) + l32 * L::RPITCH + 16 * h;
+            bf16x8 fa[KS];
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) fa[ks] = *(const LDS bf16x8*)(srow + 32 * ks);
             f32x16 x = (f32x16){};
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) x = mfma32(*(const LDS bf16x8*)(srow + 32 * ks), rf[ks], x);
+            for (int ks = 0; ks < KS; ++ks) x = mfma32(fa[ks], rf[ks], x);
+            reads_ahead<KS>();
             if (!dk_role) {            // dP out
 #pragma unroll
                 for (int qd = 0; qd < 4; ++qd)
@@ -556,21 +595,30 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(
                     zword >>= 4 * h;
                 }
                 const LDS float* st = (const LDS float*)(base + L::S);
-                bf16x8 pw[2];
+                float arg[16];
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
                     const f32x4 lse4 = *(const LDS f32x4*)(st + 8 * g + 4 * h);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int i = 4 * g + e;
-                        const int qry = row0 + 8 * g + 4 * h + e;
-                        bool dead = false;
-                        if (masked) dead = my_row >= N || qry >= N || (CAUSAL && my_row > qry);
-                        p[i] = dead ? 0.f : __builtin_amdgcn_exp2f(fmaf(x[i], c, -lse4[e]));
-                        // keep bit as a 0/1 multiplier (no condition registers held)
-                        const float keepf = DROP ? (float)((zword >> (8 * g + e)) & 1u) : 1.f;
-                        pw[i >> 3][i & 7] = (__bf16)(p[i] * keepf);
+                    for (int e = 0; e < 4; ++e) arg[4 * g + e] = fmaf(x[4 * g + e], c, -lse4[e]);
+                }
+                // Dead scores get exp2(-inf) = 0: selects under one uniform
+                // branch, not a branch around each exponential.
+                if (masked) {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int qry = row0 + 8 * (i >> 2) + 4 * h + (i & 3);
+                        const bool dead = (my_row >= N) | (qry >= N) | (CAUSAL & (my_row > qry));
+                        arg[i] = dead ? -__builtin_inff() : arg[i];
                     }
+                }
+                bf16x8 pw[2];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    p[i] = __builtin_amdgcn_exp2f(arg[i]);
+                    // keep bit as a 0/1 multiplier (no condition registers held)
+                    const float keepf = DROP ? (float)((zword >> (8 * (i >> 2) + (i & 3))) & 1u) : 1.f;
+                    pw[i >> 3][i & 7] = (__bf16)(p[i] * keepf);
                 }
                 pxp[lane] = pw[0];
                 pxp[64 + lane] = pw[1];
@@ -578,6 +626,12 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(
         }
         __syncthreads();
         if (active) {
+            // operands of dK^T += (Q^T) dS  or  dV^T += (dO^T) P, read first so
+            // that they arrive during the dS arithmetic
+            const LDS char* trow = base + (dk_role ? L::TQ : L::TO) + l32 * L::TPITCH + 16 * h;
+            bf16x8 ft[2 * DB];
+#pragma unroll
+            for (int i = 0; i < 2 * DB; ++i) ft[i] = *(const LDS bf16x8*)(trow + 32 * (i >> 1) * L::TPITCH + 32 * (i & 1));
             bf16x8 w[2];
             if (dk_role) {             // dS from the partner's dP
                 const LDS float* st = (const LDS float*)(base + L::S);
@@ -603,12 +657,8 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(
                 w[1] = pxp[64 + lane];
             }
             // dK^T += (Q^T) dS  or  dV^T += (dO^T) P
-            const LDS char* trow = base + (dk_role ? L::TQ : L::TO) + l32 * L::TPITCH + 16 * h;
 #pragma unroll
-            for (int db = 0; db < DB; ++db)
-#pragma unroll
-                for (int cc = 0; cc < 2; ++cc)
-                    acc[db] = mfma32(*(const LDS bf16x8*)(trow + 32 * db * L::TPITCH + 32 * cc), w[cc], acc[db]);
+            for (int i = 0; i < 2 * DB; ++i) acc[i >> 1] = mfma32(ft[i], w[i & 1], acc[i >> 1]);
         }
         if (step + 1 < n_steps) store_step(set ^ 1);
         __syncthreads();
