@@ -67,19 +67,19 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// Instruction order for a run of N MFMAs whose A operands are N LDS reads
-// written before them: the reads go kAhead MFMAs ahead of their use, so that
+// Instruction order for a run of N MFMAs whose A operands are N * R LDS
+// reads written before them: the reads go kAhead MFMAs ahead of their use, so that
 // an MFMA does not wait for a read issued just before it.  (Groups for the
 // scheduler: mask 0x100 = LDS reads, 0x008 = MFMAs.)
 constexpr int kAhead = 4;
-template <int N>
+template <int N, int R = 1>
 __device__ __forceinline__ void reads_ahead() {
     if constexpr (N > kAhead) {
-        __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, R * kAhead, 0);
 #pragma unroll
         for (int i = 0; i < N - kAhead; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
         }
         __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 0);
     }
@@ -90,72 +90,88 @@ __device__ __forceinline__ bool keep_half(uint32_t word, int hi, uint32_t t) {
     return (hi ? word >> 16 : word & 0xFFFFu) >= t;
 }
 
-// Permuted position of row k (0..31) of a streamed tile inside a transposed
-// LDS row: within each 16-row chunk, row 8*b3 + 4*b2 + b moves to
-// 8*b2 + 4*b3 + b.  With it, accumulator registers 8c..8c+7 of a 32x32 MFMA
-// (rows (r/4)*8 + h*4 + r%4) are the 16-element operand of chunk c.
-__device__ __forceinline__ int tr_pos(int k) {
-    return (k & ~15) | ((k & 4) << 1) | ((k & 8) >> 1) | (k & 3);
+// LDS image of one streamed tile: kTile rows of D bf16, row-major and
+// unpadded, with the 16-byte chunk c of row r at chunk position c ^ rswz(r).
+// Both ways the kernels read a tile are then free of bank conflicts (64 banks
+// of 4 bytes):
+//   - 16-byte reads of one chunk on 16 consecutive rows (an MFMA operand with
+//     one tile row per lane): rswz is one-to-one on r mod 16;
+//   - transposing 8-byte reads, 16 lanes over 4 consecutive rows and 32
+//     consecutive bytes of each (an MFMA operand with one column per lane):
+//     rows r mod 4 = 0..3 land in four different 64-byte quarters.
+// rswz depends on r mod 16 only.
+template <int D>
+__device__ __forceinline__ int rswz(int r) {
+    static_assert(D == 64 || D == 128, "head dimensions 64 and 128");
+    return D == 128 ? 4 * (r & 3) + ((r >> 2) & 3) : 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
 }
 
-// LDS layout of one buffer set.
+// LDS layout of one buffer set (dQ kernel).
 template <int D>
 struct Lay {
-    static constexpr int RPITCH = 2 * D + 16;            // row-major tile row
-    static constexpr int TPITCH = 2 * kTile + 16;        // transposed row (one d)
-    static constexpr int RBYTES = kTile * RPITCH;
-    static constexpr int TBYTES = D * TPITCH;
-    static constexpr int A = 0;                          // row-major tile 1
-    static constexpr int B = RBYTES;                     // row-major tile 2
-    static constexpr int T = 2 * RBYTES;                 // transposed tile
-    static constexpr int S = 2 * RBYTES + TBYTES;        // two float[32] rows of statistics
-    static constexpr int SET = S + 2 * kTile * 4;
+    static constexpr int RBYTES = kTile * 2 * D;
+    static constexpr int A = 0;                          // K rows
+    static constexpr int B = RBYTES;                     // V rows
+    static constexpr int SET = 2 * RBYTES;
     static constexpr int BYTES = 2 * SET;
-    static constexpr int CHUNKS = D / 8;                 // 16-byte chunks per row
-    static constexpr int ITEMS = (kTile / 2) * CHUNKS;   // (row pair, chunk) items per tile
 };
+constexpr int kHalf = kTile / 2;
 
-// Per-thread staging of one streamed tile: the item (row pair j, chunk c8)
-// of two tensors.
+// Per-thread staging of one streamed tile: chunk c8 of rows r and r + 16, for
+// item it = 16 r + c8 (D = 128; 8 r + c8 at D = 64) of each of two tensors.
+// Consecutive threads take consecutive chunks of a row, so the global loads
+// are whole rows.
 template <int D>
 struct Stage {
-    u32x4 x0, x1;     // tensor 1, rows 2j and 2j+1
-    u32x4 y0, y1;     // tensor 2, rows 2j and 2j+1
+    u32x4 x0, x1;     // tensor 1
+    u32x4 y0, y1;     // tensor 2
 };
+template <int D>
+constexpr int kItems = kHalf * (D / 8);                  // threads that copy one tile
 
 template <int D>
 __device__ __forceinline__ void stage_rows(const __bf16* __restrict__ g, int row0, int n, int tid,
                                            u32x4& r0, u32x4& r1) {
-    using L = Lay<D>;
-    const int it = tid % L::ITEMS;
-    const int j = it % (kTile / 2), c8 = it / (kTile / 2);
-    const int a = min(row0 + 2 * j, n - 1), b = min(row0 + 2 * j + 1, n - 1);
+    const int it = tid % kItems<D>;
+    const int c8 = it % (D / 8), r = it / (D / 8);
+    const int a = min(row0 + r, n - 1), b = min(row0 + r + kHalf, n - 1);
     r0 = *(const u32x4*)(g + (size_t)a * D + 8 * c8);
     r1 = *(const u32x4*)(g + (size_t)b * D + 8 * c8);
 }
 
 template <int D>
 __device__ __forceinline__ void put_rows(LDS char* dst, int tid, const u32x4& r0, const u32x4& r1) {
-    using L = Lay<D>;
-    if (tid >= L::ITEMS) return;
-    const int j = tid % (kTile / 2), c8 = tid / (kTile / 2);
-    *(LDS u32x4*)(dst + (2 * j) * L::RPITCH + 16 * c8) = r0;
-    *(LDS u32x4*)(dst + (2 * j + 1) * L::RPITCH + 16 * c8) = r1;
+    if (tid >= kItems<D>) return;
+    const int c8 = tid % (D / 8), r = tid / (D / 8);
+    const int pos = 16 * (c8 ^ rswz<D>(r));
+    *(LDS u32x4*)(dst + r * 2 * D + pos) = r0;
+    *(LDS u32x4*)(dst + (r + kHalf) * 2 * D + pos) = r1;
 }
 
+// Per-lane offsets for the two operand forms of a tile.  Row operand (lane =
+// tile row l32, d = 16 ks + 8 h .. + 7): offset rowop ^ (32 ks).  Transposed
+// operand of chunk cc (lane = d 32 db + l32, tile rows {16 cc + 4 h + 0..3,
+// 16 cc + 8 + 4 h + 0..3}, the key order of an accumulator's registers
+// 8 cc .. 8 cc + 7): two transposing reads at 32 D cc + (trop[k] ^ (64 db)),
+// k = 0, 1.  (The XORs act on the chunk bits alone: row offsets are multiples
+// of 2D and element offsets stay below 16 bytes.)
 template <int D>
-__device__ __forceinline__ void put_transposed(LDS char* dst, int tid, const u32x4& r0, const u32x4& r1) {
-    using L = Lay<D>;
-    if (tid >= L::ITEMS) return;
-    const int j = tid % (kTile / 2), c8 = tid / (kTile / 2);
-    LDS char* p = dst + 8 * c8 * L::TPITCH + tr_pos(2 * j) * 2;   // rows 2j, 2j+1 stay adjacent
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const uint32_t lo = __builtin_amdgcn_perm(r1[e], r0[e], 0x05040100u);
-        const uint32_t hi = __builtin_amdgcn_perm(r1[e], r0[e], 0x07060302u);
-        *(LDS uint32_t*)(p + (2 * e) * L::TPITCH) = lo;
-        *(LDS uint32_t*)(p + (2 * e + 1) * L::TPITCH) = hi;
-    }
+__device__ __forceinline__ int rowop_off(int lane) {
+    const int l32 = lane & 31, h = lane >> 5;
+    return l32 * 2 * D + 16 * (h ^ rswz<D>(l32));
+}
+template <int D>
+__device__ __forceinline__ int trop_off(int lane, int k) {
+    const int vr = 4 * (lane >> 5) + ((lane & 15) >> 2) + 8 * k;     // tile row of this lane's piece
+    const int dlo = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);          // its d within the 32-d block
+    return vr * 2 * D + 16 * ((dlo >> 3) ^ rswz<D>(vr)) + 2 * (dlo & 7);
+}
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+template <int D>
+__device__ __forceinline__ bf16x8 tr_operand(const LDS char* tile, int t0, int t1, int db, int cc) {
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS i16x4*)(tile + 32 * D * cc + (t0 ^ (64 * db))));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS i16x4*)(tile + 32 * D * cc + (t1 ^ (64 * db))));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 // Row statistics of the streamed query rows (dK/dV kernel): LSE * log2(e)
@@ -274,6 +290,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
 
     // Each step's copy: A = K rows, B = V rows, T = K transposed.
     Stage<D> stg;
+    const int rowop = rowop_off<D>(lane);
+    const int trop0 = trop_off<D>(lane, 0), trop1 = trop_off<D>(lane, 1);
     auto load_step = [&](int step) __attribute__((always_inline)) {
         const int row0 = min(step, n_steps - 1) * kTile;
         stage_rows<D>(K + kvhead, row0, N, tid, stg.x0, stg.x1);
@@ -283,7 +301,6 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
         LDS char* base = smem + set * L::SET;
         put_rows<D>(base + L::A, tid, stg.x0, stg.x1);
         put_rows<D>(base + L::B, tid, stg.y0, stg.y1);
-        put_transposed<D>(base + L::T, tid, stg.x0, stg.x1);
     };
 
     // n_steps >= 1: the workgroup's first row is below N, so key tile 0 is
@@ -332,13 +349,11 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
                 }
             }
             // score products: S^T and dP^T with one query per lane
-            const LDS char* arow = base + L::A + l32 * L::RPITCH + 16 * h;
-            const LDS char* brow = base + L::B + l32 * L::RPITCH + 16 * h;
             bf16x8 fa[2 * KS];
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                fa[2 * ks] = *(const LDS bf16x8*)(arow + 32 * ks);
-                fa[2 * ks + 1] = *(const LDS bf16x8*)(brow + 32 * ks);
+                fa[2 * ks] = *(const LDS bf16x8*)(base + L::A + (rowop ^ (32 * ks)));
+                fa[2 * ks + 1] = *(const LDS bf16x8*)(base + L::B + (rowop ^ (32 * ks)));
             }
             f32x16 x = (f32x16){}, y = (f32x16){};
 #pragma unroll
@@ -375,13 +390,12 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
                 w[i >> 3][i & 7] = (__bf16)val;
             }
             // dQ^T (d x queries) += (K^T) (d x keys) dS^T
-            const LDS char* trow = base + L::T + l32 * L::TPITCH + 16 * h;
             bf16x8 ft[2 * DB];
 #pragma unroll
-            for (int i = 0; i < 2 * DB; ++i) ft[i] = *(const LDS bf16x8*)(trow + 32 * (i >> 1) * L::TPITCH + 32 * (i & 1));
+            for (int i = 0; i < 2 * DB; ++i) ft[i] = tr_operand<D>(base + L::A, trop0, trop1, i >> 1, i & 1);
 #pragma unroll
             for (int i = 0; i < 2 * DB; ++i) acc[i >> 1] = mfma32(ft[i], w[i & 1], acc[i >> 1]);
-            reads_ahead<2 * DB>();
+            reads_ahead<2 * DB, 2>();
         }
         if (step + 1 < n_steps) store_step(set ^ 1);
         __syncthreads();
@@ -417,20 +431,14 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
 // for the products anyway, thinned by dropout); dP in fp32.
 template <int D>
 struct Lay2 {
-    static constexpr int RPITCH = 2 * D + 16;
-    static constexpr int TPITCH = 2 * kTile + 16;
-    static constexpr int RBYTES = kTile * RPITCH;
-    static constexpr int TBYTES = D * TPITCH;
+    static constexpr int RBYTES = kTile * 2 * D;
     static constexpr int A = 0;                           // Q rows
     static constexpr int B = RBYTES;                      // dO rows
-    static constexpr int TQ = 2 * RBYTES;                 // Q^T
-    static constexpr int TO = 2 * RBYTES + TBYTES;        // dO^T
-    static constexpr int S = 2 * RBYTES + 2 * TBYTES;     // LSE*log2e and D of the 32 rows
+    static constexpr int S = 2 * RBYTES;                  // LSE*log2e and D of the 32 rows
     static constexpr int SET = S + 2 * kTile * 4;
     static constexpr int PXP = 2 * SET;                   // P:  [4 pairs][2 chunks][64 lanes] x 16 B
     static constexpr int PXD = PXP + 4 * 2 * 64 * 16;     // dP: [4 pairs][4 quads][64 lanes] x 16 B
     static constexpr int BYTES = PXD + 4 * 4 * 64 * 16;
-    static constexpr int ITEMS = (kTile / 2) * (D / 8);
 };
 constexpr int kDkvThreads = 512;
 
@@ -516,7 +524,6 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(
     auto store_step = [&](int set) __attribute__((always_inline)) {
         LDS char* base = smem + set * L::SET;
         put_rows<D>(base + (copy_do ? L::B : L::A), ct, x0, x1);
-        put_transposed<D>(base + (copy_do ? L::TO : L::TQ), ct, x0, x1);
         if (tid < kTile) {
             float lse2, dv;
             finish_stats(s0, s1, srow, N, lse2, dv);
@@ -533,6 +540,9 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(
     __syncthreads();
 
     LDS bf16x8* pxp = (LDS bf16x8*)(smem + L::PXP) + wb * 128;   // [cc][lane]
+    const int mine = dk_role ? L::A : L::B;                      // the streamed tile this wave reads
+    const int rowop = rowop_off<D>(lane);
+    const int trop0 = trop_off<D>(lane, 0), trop1 = trop_off<D>(lane, 1);
     LDS f32x4* pxd = (LDS f32x4*)(smem + L::PXD) + wb * 256;     // [quad][lane]
 
 #pragma unroll 1
@@ -551,10 +561,9 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(
         float p[16];
         uint32_t zword = 0;
         if (active) {
-            const LDS char* srow = base + (dk_role ? L::A : L::B) + l32 * L::RPITCH + 16 * h;
             bf16x8 fa[KS];
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) fa[ks] = *(const LDS bf16x8*)(srow + 32 * ks);
+            for (int ks = 0; ks < KS; ++ks) fa[ks] = *(const LDS bf16x8*)(base + mine + (rowop ^ (32 * ks)));
             f32x16 x = (f32x16){};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) x = mfma32(fa[ks], rf[ks], x);
@@ -628,10 +637,9 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(
         if (active) {
             // operands of dK^T += (Q^T) dS  or  dV^T += (dO^T) P, read first so
             // that they arrive during the dS arithmetic
-            const LDS char* trow = base + (dk_role ? L::TQ : L::TO) + l32 * L::TPITCH + 16 * h;
             bf16x8 ft[2 * DB];
 #pragma unroll
-            for (int i = 0; i < 2 * DB; ++i) ft[i] = *(const LDS bf16x8*)(trow + 32 * (i >> 1) * L::TPITCH + 32 * (i & 1));
+            for (int i = 0; i < 2 * DB; ++i) ft[i] = tr_operand<D>(base + mine, trop0, trop1, i >> 1, i & 1);
             bf16x8 w[2];
             if (dk_role) {             // dS from the partner's dP
                 const LDS float* st = (const LDS float*)(base + L::S);
