@@ -76,6 +76,15 @@ SMALL = [
     # 32 and 64 query heads: the XCD work order that takes heads four at a time
     Workload("h32-gqa-ragged", 1, 32, 8, 300, 64, True, "bf16", 72),
     Workload("h64-noncausal-ragged", 2, 32, 32, 130, 128, False, "bf16", 73),
+    # More query tiles than compute units: resident workgroups that walk
+    # several items each, with the next item's Q rows and first K tile loaded
+    # during the current one.  One case per head-count branch of the work
+    # order (multiple of 32, multiple of 8, neither), ragged tails, GQA.
+    Workload("resident-h64-gqa-ragged", 1, 64, 16, 1100, 128, True, "bf16", 74),
+    Workload("resident-h72-gqa-ragged", 3, 24, 6, 1100, 128, True, "bf16", 75),
+    Workload("resident-h37-d64-ragged", 1, 37, 37, 2000, 64, True, "bf16", 76),
+    Workload("resident-h80-noncausal-d64", 2, 40, 40, 900, 64, False, "bf16", 77),
+    Workload("resident-h36-noncausal-ragged", 1, 36, 12, 2000, 128, False, "bf16", 78),
 ]
 
 
