@@ -520,7 +520,13 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
         grp = pos >> 2;
         idx = pos & 3;
     }
-    const int rblock = 2 * idx + grp;         // the groups interleave 32-row blocks
+    // Row blocks: the first group takes blocks 0..3 and the second 7..4, so
+    // SIMD k holds blocks k and 7 - k.  On the diagonal of a causal tile the
+    // blocks need 1, 1, 2, 2, 3, 3, 4, 4 of its four key tiles; paired this
+    // way, each SIMD has one working wave in the last two diagonal steps
+    // (instead of one SIMD with two and two SIMDs with none), and a wave
+    // alone on its SIMD runs its phase faster.
+    const int rblock = grp == 0 ? idx : kWaves - 1 - idx;
 
     const size_t q_head = (size_t)bh * N * D;
     const int q0 = qt * kBr;
