@@ -122,6 +122,28 @@ def test_parity_full_size_sampled_rows(name):
          f"max|dLSE|={lmx:.3e}")
 
 
+LONG = [
+    # 16384 key tiles for the last rows, ragged tail, one query head
+    Workload("long-causal-d128", 1, 1, 1, (1 << 20) - 3, 128, True, "bf16", 91),
+    # GQA pair at d = 64, non-causal, ragged
+    Workload("long-noncausal-d64-gqa", 1, 2, 1, (1 << 17) + 1, 64, False, "bf16", 92),
+]
+
+
+@pytest.mark.parametrize("w", LONG, ids=lambda w: w.name)
+def test_long_sequences_sampled_rows(w):
+    """Long sequences (far more key tiles per row than any configuration): the
+    sampled rows of every head against the oracle.  The interface admits N up
+    to 2^23; a causal head at that length is about 2e16 FLOPs (many seconds)
+    and 2 GiB per input, so the test stops at 2^20."""
+    q, k, v, o, lse = _run(w)
+    rows = _sample_rows(w, n_random=4)
+    o_ref, lse_ref = oracle.attention_rows(q, k, v, w.causal, w.scale, rows)
+    idx = tuple(np.array(rows).T)
+    mx, mean, lmx = _check(w, o[idx], lse[idx], o_ref, lse_ref)
+    _say(f"{w.name} sampled {len(rows)} rows: max|dO|={mx:.3e} mean|dO|={mean:.3e} max|dLSE|={lmx:.3e}")
+
+
 @pytest.mark.parametrize("name", ["c3", "c5"])
 def test_full_size_constant_scores_closed_form(name):
     """Q = 0 (exact in bf16): every allowed key has weight 1/(i+1), so
