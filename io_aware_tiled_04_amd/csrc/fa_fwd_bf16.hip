@@ -317,13 +317,18 @@ __device__ __forceinline__ void gemm_phase(const LDS char* vl, const LDS char* k
 template <int D>
 __device__ __forceinline__ float exp_tile(const f32x16 (&s)[Tile<D>::KB], bf16x8 (&pb)[Tile<D>::BC / 16],
                                           float m_use, float c_log2) {
-    float ps[4] = {0.f, 0.f, 0.f, 0.f};
+    // four partial sums, seeded with the first four weights (p >= 0, so this
+    // equals summing from zero)
+    float ps[4];
 #pragma unroll
     for (int kb = 0; kb < Tile<D>::KB; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][i], c_log2, -m_use));
-            ps[i & 3] += p;
+            if (kb == 0 && i < 4)
+                ps[i] = p;
+            else
+                ps[i & 3] += p;
             pb[2 * kb + (i >> 3)][i & 7] = (__bf16)p;
         }
     return (ps[0] + ps[1]) + (ps[2] + ps[3]);
