@@ -96,9 +96,10 @@ def cpu_baseline(w, q, k, v, budget_s: float):
                       f"(the oracle computes all N^2 scores)"}
 
 
-def summarize(d: str) -> None:
+def summarize(d: str, skip: int = 0) -> None:
     """Per-kernel figures from a rocprofv3 output directory (its rocpd SQLite
-    database): average dispatch duration from a kernel trace, and per-dispatch
+    database): average dispatch duration from a kernel trace (leaving out
+    each kernel's first ``skip`` dispatches, the warm-up), and per-dispatch
     counter values from a --pmc run, with the FETCH_SIZE / WRITE_SIZE scale
     factors implied by the elementwise copy of --calibrate-copy (which reads
     and writes COPY_BYTES each)."""
@@ -106,13 +107,16 @@ def summarize(d: str) -> None:
     for path in sorted(glob.glob(os.path.join(d, "**", "*_results.db"), recursive=True)):
         con = sqlite3.connect(path)
         views = {r[0] for r in con.execute("select name from sqlite_master")}
-        print(f"# {os.path.relpath(path, d)}")
+        print(f"# {os.path.relpath(path, d)}" + (f" (first {skip} dispatches of each kernel left out)"
+                                                  if skip else ""))
         if "kernels" in views:
-            for name, n, avg, mn, mx in con.execute(
-                    "select name, count(*), avg(duration), min(duration), max(duration) "
-                    "from kernels group by name order by sum(duration) desc"):
-                print(f"trace | {name[:80]} | calls={n} avg_us={avg / 1e3:.2f} "
-                      f"min_us={mn / 1e3:.2f} max_us={mx / 1e3:.2f}")
+            per = {}
+            for name, dur in con.execute("select name, duration from kernels order by start"):
+                per.setdefault(name, []).append(dur)
+            for name, durs in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+                kept = durs[skip:] if len(durs) > skip else durs
+                print(f"trace | {name[:80]} | calls={len(kept)} avg_us={sum(kept) / len(kept) / 1e3:.2f} "
+                      f"min_us={min(kept) / 1e3:.2f} max_us={max(kept) / 1e3:.2f}")
         if "counters_collection" in views:
             rows = list(con.execute(
                 "select kernel_name, counter_name, count(*), avg(value), min(value), max(value) "
@@ -133,14 +137,19 @@ def summarize(d: str) -> None:
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    # The shader clock ramps up over roughly the first 100 launches of the
+    # forward kernel (launch time falls from about 310 to 265 us on c3, then
+    # stays flat), so the default warm-up covers that ramp.
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--config", default=None,
                     help="workload (default c3; s1 with --splitkv)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--summarize", default=None)
+    ap.add_argument("--skip", type=int, default=0,
+                    help="with --summarize: leave out each kernel's first SKIP dispatches (the warm-up)")
     ap.add_argument("--splitkv", type=int, default=0,
                     help="time fa_fwd_splitkv with this many splits (and fa_fwd beside it)")
     ap.add_argument("--backward", action="store_true", help="time the backward pass (fa_bwd)")
@@ -151,7 +160,7 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.summarize:
-        summarize(args.summarize)
+        summarize(args.summarize, args.skip)
         return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this forward pass shards over (batch, head) "
