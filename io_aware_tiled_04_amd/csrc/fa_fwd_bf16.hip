@@ -29,10 +29,11 @@
 //    raises its issue priority for its matrix phase.
 //  * Direct global-to-LDS copies.  K and V tiles go from HBM straight into
 //    LDS (buffer loads with the LDS flag, no registers, no LDS store
-//    instructions): the second group loads K tiles and the first group V
-//    tiles, each at the end of its matrix phase, into buffer rings deep
-//    enough that the target is free.  Rows past the end of the sequence come
-//    back as zeros from the buffer range check.
+//    instructions): the second group loads K tiles at the start of its
+//    vector phase and the first group V tiles at the start of its matrix
+//    phase, into two-deep rings whose target buffer the preceding barrier has
+//    just freed.  Rows past the end of the sequence come back as zeros from
+//    the buffer range check.
 // and one change against a literal reading, exact in real arithmetic:
 //  * Lazy rescaling.  The reference max m of a row is the exact row max of
 //    the first tile; afterwards P is taken against it directly, and m only
