@@ -40,9 +40,17 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_bf16_c3_hbm_traffic.md")
 COPY_BYTES = 512 << 20
 
 
-def kernel_sha() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def kernel_sha(text=None) -> str:
+    """Hash of the kernel source's code: comments and whitespace are left out,
+    so that a change of wording does not count as a change of the kernel."""
+    import re
+    if text is None:
+        with open(KERNEL_SRC, encoding="utf-8") as f:
+            text = f.read()
+    code = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    code = re.sub(r"//[^\n]*", " ", code)
+    code = " ".join(code.split())
+    return hashlib.sha256(code.encode("utf-8")).hexdigest()[:16]
 
 
 def read_traffic():
