@@ -178,6 +178,29 @@ def test_first_causal_row_is_v0():
     assert np.max(np.abs(lse[:, :, 0] - ref)) <= TOL_LSE
 
 
+@pytest.mark.parametrize("slope", [0.5, -0.5])
+@pytest.mark.parametrize("causal", [True, False])
+def test_logits_that_move_every_tile(slope, causal):
+    """Scaled logits that rise (or fall) by 0.5 per key.  Rising, every
+    64-key tile's max exceeds the reference of the tiles before by about 46
+    in log2 units, so every tile takes the exact-max redo with a rescale of O
+    and l; falling, the first tile's reference holds and the later weights
+    underflow to zero.  Q is zero but for one column of ones (exact in
+    bf16), so the logits come from that column of K alone."""
+    w = Workload("moving-max", 1, 2, 1, 1000, 128, causal, "bf16", 85)
+    g = torch.Generator().manual_seed(85)
+    q = torch.zeros(w.B, w.Hq, w.N, w.d)
+    q[..., 0] = 1.0
+    k = 0.1 * torch.randn(w.B, w.Hkv, w.N, w.d, generator=g)
+    k[..., 0] = slope * torch.arange(w.N, dtype=torch.float32) / w.scale
+    v = torch.randn(w.B, w.Hkv, w.N, w.d, generator=g)
+    q, k, v = (t.to(torch.bfloat16) for t in (q, k, v))
+    q64, k64, v64, o, lse = _run(w, q, k, v)
+    o_ref, lse_ref = oracle.attention_ref(q64, k64, v64, w.causal, w.scale)
+    mx, mean, lmx = _check(w, o, lse, o_ref, lse_ref)
+    _say(f"moving max slope={slope} causal={causal}: max|dO|={mx:.3e} mean|dO|={mean:.3e} max|dLSE|={lmx:.3e}")
+
+
 def test_gqa_equals_mha_bitwise():
     """The GQA head map equals plain multi-head attention on K/V repeated per
     group, bit for bit."""
