@@ -263,6 +263,9 @@ __device__ __forceinline__ void gemm_phase(const LDS char* vl, const LDS char* k
     constexpr int NPV = HAS_PV ? (T::BC / 16) * DB : 0;
     constexpr int NS = HAS_S ? (D / 16) * T::KB : 0;
     constexpr int NF = NPV + NS;
+    // Operands 0 .. NS-1 are those of S^T = K Q^T, then those of the P V
+    // product: the S accumulators are complete first, so the wave's next
+    // (vector) phase can start on them while the P V MFMAs drain.
     const int h = lane >> 5;
     const int l32 = lane & 31;
     const LDS char* krow = kl + (h * T::BC + l32) * 16;     // chunk h, key l32
@@ -271,15 +274,16 @@ __device__ __forceinline__ void gemm_phase(const LDS char* vl, const LDS char* k
     bf16x8 fr[NF > 0 ? NF : 1];
 #pragma unroll
     for (int i = 0; i < NF; ++i) {
-        if (i < NPV) {
-            const int cc = i / DB, db = i % DB;
+        if (i >= NS) {
+            const int j = i - NS;
+            const int cc = j / DB, db = j % DB;
             const LDS char* vp = vl + (16 * cc + vr) * (2 * D) + 16 * ((4 * db + dlo / 8) ^ vswz<D>(vr)) +
                                  2 * (dlo % 8);
             const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS i16x4*)vp);
             const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS i16x4*)(vp + 8 * (2 * D)));
             fr[i] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         } else {
-            const int ks = (i - NPV) / T::KB, kb = (i - NPV) % T::KB;
+            const int ks = i / T::KB, kb = i % T::KB;
             fr[i] = *(const LDS bf16x8*)(krow + (2 * ks * T::BC + 32 * kb) * 16);
         }
     }
@@ -289,22 +293,23 @@ __device__ __forceinline__ void gemm_phase(const LDS char* vl, const LDS char* k
     }
 #pragma unroll
     for (int i = 0; i < NF; ++i) {
-        if (i < NPV) {
-            const int cc = i / DB, db = i % DB;
+        if (i >= NS) {
+            const int j = i - NS;
+            const int cc = j / DB, db = j % DB;
             oacc[db] = mfma32(fr[i], pb[cc], oacc[db]);
         } else {
-            const int ks = (i - NPV) / T::KB, kb = (i - NPV) % T::KB;
+            const int ks = i / T::KB, kb = i % T::KB;
             s[kb] = mfma32(fr[i], qf[ks], s[kb]);
         }
     }
     // A P V operand takes two reads, an S operand one.
     if constexpr (NF > kAhead) {
-        constexpr int first_reads = NPV >= kAhead ? 2 * kAhead : 2 * NPV + (kAhead - NPV);
+        constexpr int first_reads = NS >= kAhead ? kAhead : NS + 2 * (kAhead - NS);
         __builtin_amdgcn_sched_group_barrier(kSchedDsRead, first_reads, 0);
 #pragma unroll
         for (int i = 0; i < NF - kAhead; ++i) {
             __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-            if (i + kAhead < NPV)
+            if (i + kAhead >= NS)
                 __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
             else
                 __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
