@@ -22,7 +22,7 @@
 // Scheduling choices (the arithmetic is that of the method):
 //  * Ping-pong.  The 8 waves form two groups with one wave of each on every
 //    SIMD.  Between workgroup barriers, one group runs a matrix phase
-//    (P_{t-1} V_{t-1} and S_t) while the other runs a vector phase (the
+//    (S_t and P_{t-1} V_{t-1}) while the other runs a vector phase (the
 //    softmax of its S), then they swap, so the matrix cores of each SIMD are
 //    fed by one group while the other keeps the vector ALUs busy.  K tiles
 //    run one tile ahead of V tiles through LDS to fit this order.  A wave
@@ -230,8 +230,8 @@ __device__ __forceinline__ void dma_v(u32x4 rv, LDS char* buf, int key0, int idx
     }
 }
 
-// The matrix phase of one tile step: O^T += V^T P^T for the previous tile
-// (HAS_PV) and S^T = K Q^T for the current one (HAS_S), as one stream of LDS
+// The matrix phase of one tile step: S^T = K Q^T for the current tile
+// (HAS_S) and O^T += V^T P^T for the previous one (HAS_PV), as one stream of LDS
 // operand reads and MFMAs.  The reads run kAhead MFMAs ahead of their use
 // (scheduling groups below), so the LDS latency stays hidden behind the
 // matrix core instead of stalling every MFMA.
@@ -599,7 +599,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
 
     // Phases p = 0 .. 2*n_tiles+1, each closed by a workgroup barrier.  The
     // group's local phase lp = p - grp: even lp = 2t is the matrix phase t
-    // (P_{t-1} V_{t-1}, then S_t; K_t and V_{t-1} are read), odd lp = 2t+1
+    // (S_t, then P_{t-1} V_{t-1}; K_t and V_{t-1} are read), odd lp = 2t+1
     // the softmax of S_t.
     auto matrix_phase = [&](int t) __attribute__((always_inline)) {
         const bool has_pv = t >= 1 && t - 1 < w_tiles;
