@@ -313,3 +313,47 @@ def test_side_stream():
     s.synchronize()
     o_ref, lse_ref = oracle.attention_ref(*(as_f64_numpy(t) for t in (q, k, v)), True, w.scale)
     _check(w, as_f64_numpy(o), as_f64_numpy(lse), o_ref, lse_ref)
+
+
+def test_concurrent_streams_and_host_threads():
+    """Two different problems launched at once, from two host threads, each on
+    its own stream (both at the default priority), give bit for bit the
+    results of running each alone: the library keeps no state between calls."""
+    import threading
+    fa = _fa()
+    ws = [Workload("conc-a", 2, 8, 2, 1500, 128, True, "bf16", 86),
+          Workload("conc-b", 1, 16, 16, 700, 64, False, "bf16", 87)]
+    ins = [tuple(t.cuda() for t in make_inputs(w)) for w in ws]
+    _say("concurrent streams: serial reference")
+    alone = []
+    for w, (q, k, v) in zip(ws, ins):
+        alone.append(fa.fwd(q, k, v, causal=w.causal, scale=w.scale))
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in ws]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    outs = [None] * len(ws)
+    errors = []
+
+    def run(i):
+        try:
+            with torch.cuda.stream(streams[i]):
+                q, k, v = ins[i]
+                res = []
+                for _ in range(5):
+                    res.append(fa.fwd(q, k, v, causal=ws[i].causal, scale=ws[i].scale, stream=streams[i]))
+                outs[i] = res
+        except Exception as e:  # pragma: no cover
+            errors.append(e)
+
+    _say("concurrent streams: two host threads")
+    threads = [threading.Thread(target=run, args=(i,)) for i in range(len(ws))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for i in range(len(ws)):
+        for o, lse in outs[i]:
+            assert torch.equal(o, alone[i][0]) and torch.equal(lse, alone[i][1]), ws[i].name
