@@ -112,9 +112,19 @@ __device__ __forceinline__ void lds_barrier() {
 //    P V operand is read with transposing 8-byte reads (ds_read_b64_tr_b16);
 //    a half wave's read covers 4 consecutive keys x 64 bytes, and the
 //    permutation puts those 4 rows on disjoint banks.
+// Keys per tile: one K/V tile is the work of one tile step.  At d = 64 a
+// step of 64 keys is only 16 MFMAs per wave and phase, so the fixed cost of
+// a phase (barrier, first operand reads, the other group's vector work
+// starting) weighs twice as much; 128-key tiles halve it and still fit the
+// registers (at d = 128 they do not).
+template <int D>
+constexpr int kKeyTile = 64;
+template <>
+constexpr int kKeyTile<64> = 128;
+
 template <int D>
 struct Tile {
-    static constexpr int BC = 64;                 // keys per tile
+    static constexpr int BC = kKeyTile<D>;        // keys per tile
     static constexpr int KB = BC / 32;            // 32-key blocks per tile
     static constexpr int ROW_CHUNKS = D / 8;      // 16-byte chunks per row
     static constexpr int KBYTES = BC * D * 2;
@@ -123,15 +133,18 @@ struct Tile {
     static constexpr int VBASE = NBUF * KBYTES;
     static constexpr int ROLE = VBASE + NBUF * VBYTES;   // 16 ints for the wave roles
     static constexpr int LDS_BYTES = ROLE + 64;
-    // Direct loads per wave: the K group's 4 waves load a K tile (ROW_CHUNKS
-    // loads), the V group's 4 waves a V tile (VBYTES / 1024 loads of V_ROWS
-    // whole keys each).
-    static constexpr int K_DMA = ROW_CHUNKS / 4;
+    // Direct loads per tile: a K load fills 64 keys of one chunk column
+    // (KH = BC / 64 loads per column), a V load 1 KiB of whole keys (V_ROWS
+    // keys).  The K group's 4 waves share a K tile, the V group's 4 waves a V
+    // tile.
+    static constexpr int KH = BC / 64;
+    static constexpr int KLOADS = ROW_CHUNKS * KH;
+    static constexpr int K_DMA = KLOADS / 4;
     static constexpr int V_ROWS = 1024 / (2 * D);
     static constexpr int V_DMA = VBYTES / 1024 / 4;
-    static_assert(BC == 64, "a direct K load covers one chunk of 64 keys");
-    static_assert(ROW_CHUNKS % 4 == 0 && (VBYTES / 1024) % 4 == 0, "tiles must split evenly over a wave group");
-    static_assert(ROW_CHUNKS % kWaves == 0, "the first K tile splits evenly over all waves");
+    static_assert(BC % 64 == 0, "a direct K load covers 64 keys of one chunk column");
+    static_assert(KLOADS % 4 == 0 && (VBYTES / 1024) % 4 == 0, "tiles must split evenly over a wave group");
+    static_assert(KLOADS % kWaves == 0, "the first K tile splits evenly over all waves");
 };
 
 // Chunk permutation of V row r (in 16-byte chunks).  The transposing read of
@@ -199,17 +212,23 @@ __device__ __forceinline__ float half_swap_max(float x) {
 // values they turn the role branches into scalar branches, and the register
 // allocation of the two roles' code then spills.)
 
-// K tile with first key key0 into `buf`: wave idx of the K group loads chunk
-// columns idx * K_DMA .. +K_DMA-1, lane L fetching key key0 + L.
+// Load n (0 <= n < KLOADS) of the K tile with first key key0 into `buf`:
+// keys key0 + 64 j .. +63 (j = n % KH) of chunk column c = n / KH, lane L
+// fetching key key0 + 64 j + L into slot c * BC + 64 j + L.
+template <int D>
+__device__ __forceinline__ void dma_k_load(u32x4 rk, LDS char* buf, int key0, int n, int lane) {
+    using T = Tile<D>;
+    const int c = n / T::KH, j = n % T::KH;
+    dma16(buf + c * (T::BC * 16) + j * 1024, rk, lane * (2 * D), (key0 + 64 * j) * (2 * D) + 16 * c);
+}
+// K tile with first key key0 into `buf`: wave idx of the K group issues
+// loads idx * K_DMA .. +K_DMA-1.
 template <int D>
 __device__ __forceinline__ void dma_k(u32x4 rk, LDS char* buf, int key0, int idx, int lane) {
     using T = Tile<D>;
     const int widx = __builtin_amdgcn_readfirstlane(idx);
 #pragma unroll
-    for (int i = 0; i < T::K_DMA; ++i) {
-        const int c = widx * T::K_DMA + i;
-        dma16(buf + c * (T::BC * 16), rk, lane * (2 * D), key0 * (2 * D) + 16 * c);
-    }
+    for (int i = 0; i < T::K_DMA; ++i) dma_k_load<D>(rk, buf, key0, widx * T::K_DMA + i, lane);
 }
 
 // V tile with first key key0 into `buf`: wave idx of the V group issues
@@ -503,10 +522,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     if (n_tiles > 0) {
         const int w0 = __builtin_amdgcn_readfirstlane(wave);
 #pragma unroll
-        for (int i = 0; i < T::ROW_CHUNKS / kWaves; ++i) {
-            const int c = w0 * (T::ROW_CHUNKS / kWaves) + i;
-            dma16(smem + c * (T::BC * 16), rk, lane * (2 * D), 16 * c);
-        }
+        for (int i = 0; i < T::KLOADS / kWaves; ++i) dma_k_load<D>(rk, smem, 0, w0 * (T::KLOADS / kWaves) + i, lane);
     }
 
     // Wave roles.  Order the waves by (rank among the waves on the same SIMD,

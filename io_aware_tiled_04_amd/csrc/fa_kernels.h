@@ -74,7 +74,8 @@ constexpr int kBlockRowsF32 = 64;
 constexpr int kMaxSeqLen = 1 << 23;
 // Resident rows per workgroup of the backward kernels.
 constexpr int kBwdBlockRows = 128;
-// Keys per tile of the bf16 kernel (the granularity of split-KV ranges).
+// Keys per tile of the K/V-outer kernel (the bf16 forward's key tile at
+// d = 128; at d = 64 the forward takes 128 keys per tile).
 constexpr int kKeyTileBf16 = 64;
 // Largest split count of the split-KV entry point.
 constexpr int kMaxSplits = 256;
