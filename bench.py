@@ -97,11 +97,105 @@ def cpu_baseline(w, q, k, v, budget_s: float):
         heads += 1
     dt = time.perf_counter() - t0
     return {"value": per_head * heads / dt / 1e12, "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "host_cpus": os.cpu_count(), "cpu_model": cpu_model(),
+            "threads_note": "matrix products on the BLAS threads counted in cores; numpy's exp "
+                            "and elementwise passes on one thread",
             "sample": f"{heads} of {w.B * w.Hq} whole (batch, head) units of {w.name}, "
                       f"N={w.N} d={w.d}, "
                       f"fp64 numpy, {dt:.1f} s; nominal FLOPs as for the GPU "
                       f"(the oracle computes all N^2 scores)"}
+
+
+def cpu_model() -> str | None:
+    """The host CPU's model name (from /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo", encoding="utf-8") as f:
+            for line in f:
+                if line.lower().startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+class ClockSampler:
+    """Samples the GPU's shader (gfx) clock in a background thread while the
+    timed launches run, through the AMD SMI library's metrics table (or the
+    sysfs DPM table when that is not available).  Reads only: it changes no
+    clock or power setting.  ``mhz`` is None when no source is readable."""
+
+    def __init__(self, period_s: float = 0.002):
+        import threading
+        self.period = period_s
+        self.samples = []
+        self.source = None
+        self._stop = threading.Event()
+        self._thread = None
+        self._read = self._pick_source()
+
+    def _pick_source(self):
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            handle = amdsmi.amdsmi_get_processor_handles()[0]
+
+            def read_smi():
+                m = amdsmi.amdsmi_get_gpu_metrics_info(handle)
+                for key in ("current_gfxclk", "average_gfxclk_frequency"):
+                    v = m.get(key)
+                    if isinstance(v, (int, float)) and 0 < v < 10000:
+                        return float(v)
+                clks = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, (int, float))
+                        and 0 < c < 10000]
+                return sum(clks) / len(clks) if clks else None
+
+            if read_smi() is not None:
+                self.source = "amdsmi gpu_metrics"
+                return read_smi
+        except Exception:
+            pass
+        for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+            def read_sysfs(path=path):
+                with open(path, encoding="utf-8") as f:
+                    for line in f:
+                        if line.rstrip().endswith("*"):
+                            return float(line.split(":")[1].strip().rstrip("*").strip().lower()
+                                         .replace("mhz", ""))
+                return None
+            try:
+                if read_sysfs() is not None:
+                    self.source = "sysfs pp_dpm_sclk"
+                    return read_sysfs
+            except Exception:
+                continue
+        return None
+
+    def _loop(self):
+        while not self._stop.is_set():
+            try:
+                v = self._read()
+                if v is not None:
+                    self.samples.append(v)
+            except Exception:
+                pass
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        import threading
+        if self._read is not None:
+            self._thread = threading.Thread(target=self._loop, daemon=True)
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self._thread is not None:
+            self._thread.join()
+        return False
+
+    @property
+    def mhz(self):
+        return sum(self.samples) / len(self.samples) if self.samples else None
 
 
 def summarize(d: str, skip: int = 0) -> None:
@@ -219,15 +313,16 @@ def main() -> int:
     region0 = torch.cuda.Event(enable_timing=True)
     region1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    region0.record(stream)
-    for i in range(args.steps):
-        starts[i].record(stream)
-        launch()
-        ends[i].record(stream)
-    region1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
+    with ClockSampler() as clock:
+        wall0 = time.perf_counter()
+        region0.record(stream)
+        for i in range(args.steps):
+            starts[i].record(stream)
+            launch()
+            ends[i].record(stream)
+        region1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
     total_ms = region0.elapsed_time(region1)
     launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     avg_launch_ms = sum(launch_ms) / len(launch_ms)
@@ -251,6 +346,16 @@ def main() -> int:
     flops = w.nominal_flops()
     value = flops * args.steps / (total_ms * 1e-3) / 1e12
     achieved = flops / (avg_launch_ms * 1e-3) / 1e12
+    # The shader clock ramps up over roughly the first 100 launches of a
+    # process; the first and last few launches of the timed region show
+    # where in that ramp the region sits.
+    n_edge = min(5, len(launch_ms))
+    first_us = 1e3 * sum(launch_ms[:n_edge]) / n_edge
+    last_us = 1e3 * sum(launch_ms[-n_edge:]) / n_edge
+    # Peak at the sampled clock: 256 CUs x 4 SIMDs x 1024 bf16 FLOP per clock
+    # per SIMD (the published 2.5 PFLOP/s is this at 2.4 GHz).
+    clk = clock.mhz
+    clock_peak = 256 * 4 * 1024 * clk * 1e6 / 1e12 if clk else None
     # the committed counter summary covers the headline workload only
     traffic = read_traffic() if w.name == "c3" else None
     out = {
@@ -275,7 +380,15 @@ def main() -> int:
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                      "kernel": f"fwd_bf16_kernel<{w.d}, {'causal' if w.causal else 'full'}>",
                      "avg_launch_us": round(avg_launch_ms * 1e3, 2),
-                     "min_launch_us": round(min(launch_ms) * 1e3, 2)},
+                     "min_launch_us": round(min(launch_ms) * 1e3, 2),
+                     "first5_launch_us": round(first_us, 2),
+                     "last5_launch_us": round(last_us, 2),
+                     "last5_tflops": round(flops / (last_us * 1e-6) / 1e12, 2),
+                     "sclk_mhz": round(clk, 1) if clk else None,
+                     "sclk_source": clock.source,
+                     "sclk_samples": len(clock.samples),
+                     "peak_at_sclk": round(clock_peak, 1) if clock_peak else None,
+                     "frac_at_sclk": round(achieved / clock_peak, 4) if clock_peak else None},
         "parity": {"rows": len(rows), "max_abs_o": float(err.max()),
                    "mean_abs_o": float(err.mean()), "max_abs_lse": float(lerr.max()),
                    "ok": parity_ok},
@@ -605,27 +718,32 @@ def bench_backward(args) -> int:
             raise fa.FaError(rc)
 
     avg_ms, total_ms = _time_launches(launch, stream, args.steps, args.warmup)
-    # parity on sampled query rows of dQ (each row of dQ needs only its own row of P)
-    rng = np.random.default_rng(0)
+    # parity of the first GQA group of batch 0 (its query heads and its K/V
+    # head) against the oracle's gradients; tolerances relative to each
+    # gradient's magnitude, as in the backward tests
     q64, k64, v64, do64 = (as_f64_numpy(t) for t in (q, k, v, do))
-    b, h = 0, 0
-    hk = h // (w.Hq // w.Hkv)
-    rows = np.unique(np.concatenate([[0, w.N - 1], rng.integers(0, w.N, 14)]))
-    s = w.scale * (q64[b, h, rows] @ k64[b, hk].T)
-    if w.causal:
-        s = np.where(np.arange(w.N)[None, :] > rows[:, None], -np.inf, s)
-    p = np.exp(s - s.max(axis=1, keepdims=True))
-    p /= p.sum(axis=1, keepdims=True)
-    # dropout: the oracle's keep bits of these rows, times 1/(1-p)
-    zf = (oracle.dropout_keep(seed, offset, b * w.Hq + h, rows, w.N, pdrop) / (1.0 - float(np.float32(pdrop)))
-          if pdrop else 1.0)
-    o_rows = (p * zf) @ v64[b, hk]
-    dp = (do64[b, h, rows] @ v64[b, hk].T) * zf
-    ds = p * (dp - np.sum(do64[b, h, rows] * o_rows, axis=1)[:, None])
-    dq_ref = w.scale * (ds @ k64[b, hk])
-    err = np.abs(as_f64_numpy(dq)[b, h, rows] - dq_ref)
-    mag = max(float(np.abs(dq_ref).max()), 1e-4)
-    ok = bool(err.max() <= 2e-2 * mag)
+    g = w.Hq // w.Hkv
+    dk_ref = np.zeros_like(k64[0, 0])
+    dv_ref = np.zeros_like(v64[0, 0])
+    rel = []
+    for h in range(g):
+        if pdrop:
+            gq, gk, gv = oracle.attention_dropout_backward_head(q64[0, h], k64[0, 0], v64[0, 0], do64[0, h],
+                                                                w.scale, w.causal, pdrop, seed, offset, h)
+        else:
+            gq, gk, gv = oracle.attention_backward_head(q64[0, h], k64[0, 0], v64[0, 0], do64[0, h],
+                                                        w.scale, w.causal)
+        dk_ref += gk
+        dv_ref += gv
+        rel.append(("dq", as_f64_numpy(dq[0, h]), gq))
+    rel += [("dk", as_f64_numpy(dk[0, 0]), dk_ref), ("dv", as_f64_numpy(dv[0, 0]), dv_ref)]
+    worst = {}
+    ok = True
+    for name_, got, ref in rel:
+        mag = max(float(np.abs(ref).max()), 1e-4)
+        e = np.abs(got - ref)
+        worst[name_] = max(worst.get(name_, 0.0), float(e.max() / mag))
+        ok = ok and bool(e.max() <= 2e-2 * mag and e.mean() <= 2e-3 * mag)
     flops = 2.5 * w.nominal_flops()
     out = {
         "metric": "attention bwd TFLOP/s (bf16, nominal 2.5x forward FLOPs)"
@@ -639,7 +757,7 @@ def bench_backward(args) -> int:
                    "flops_per_step": flops},
         "avg_launch_us": round(avg_ms * 1e3, 2),
         "pct_of_peak": round(100 * flops / (avg_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
-        "parity": {"rows": int(len(rows)), "max_abs_dq_rel": float(err.max() / mag), "ok": ok},
+        "parity": {"heads": g, "max_abs_rel": worst, "ok": ok},
     }
     print(json.dumps(out), flush=True)
     return 0 if ok else 1

@@ -63,7 +63,7 @@ enum fa_status {
     FA_ERR_HEADDIM = -4,   /* d is not one of the supported head sizes (64, 128) */
     FA_ERR_ARG = -5,       /* scale is not finite, num_splits or p_drop is out of range */
     FA_ERR_HIP = -6,       /* the HIP runtime rejected the launch */
-    FA_ERR_WORKSPACE = -7  /* a workspace argument is null or too small */
+    FA_ERR_WORKSPACE = -7  /* a workspace argument is null, misaligned or too small */
 };
 
 /*
@@ -116,11 +116,11 @@ size_t fa_fwd_splitkv_workspace_size(int B, int Hq, int N, int d, int num_splits
  *
  * Arguments q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, stream: as for
  *   fa_fwd (bf16 inputs and output, float32 lse).
- * num_splits: 1..256.  The keys are cut into T = ceil(N/64) tiles of 64
- *   keys, and the splits take consecutive ranges of them: with q = T /
- *   num_splits and r = T % num_splits, the first r splits take q + 1 tiles
- *   and the others q.  More splits than tiles leave some ranges empty, which
- *   is allowed.
+ * num_splits: 1..256.  The keys are cut into T = ceil(N/BC) tiles of BC
+ *   keys, the kernel's key tile: BC = 64 at d = 128 and BC = 128 at d = 64.
+ *   The splits take consecutive ranges of them: with q = T / num_splits and
+ *   r = T % num_splits, the first r splits take q + 1 tiles and the others
+ *   q.  More splits than tiles leave some ranges empty, which is allowed.
  * workspace: device memory of at least workspace_bytes bytes, owned by the
  *   caller, 16-byte aligned; workspace_bytes must be at least
  *   fa_fwd_splitkv_workspace_size(B, Hq, N, d, num_splits).  Its contents on
@@ -128,7 +128,7 @@ size_t fa_fwd_splitkv_workspace_size(int B, int Hq, int N, int d, int num_splits
  *   call that runs at the same time.
  * Both kernels are enqueued on `stream`; the library allocates nothing.
  * Returns FA_OK or a negative fa_status (FA_ERR_ARG for num_splits,
- * FA_ERR_WORKSPACE for a null or small workspace).
+ * FA_ERR_WORKSPACE for a null, misaligned or small workspace).
  */
 int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
                    int B, int Hq, int Hkv, int N, int d, int causal, float scale,

@@ -107,7 +107,8 @@ int validate_split(int B, int Hq, int N, int d, int num_splits, const void* work
     const long long bh = (long long)B * Hq;
     const long long qtiles = ((long long)N + fa::kBlockRowsBf16 - 1) / fa::kBlockRowsBf16;
     if (bh * qtiles * num_splits > INT_MAX) return FA_ERR_SHAPE;
-    if (!workspace) return FA_ERR_WORKSPACE;
+    // the split kernels store float4 values into the workspace
+    if (!workspace || ((uintptr_t)workspace & 15) != 0) return FA_ERR_WORKSPACE;
     const long long need = fa::split_workspace_floats(B, Hq, N, d, num_splits) * 4;
     if ((unsigned long long)need > (unsigned long long)workspace_bytes) return FA_ERR_WORKSPACE;
     return FA_OK;
@@ -240,7 +241,7 @@ extern "C" const char* fa_status_string(int status) {
         case FA_ERR_HEADS: return "Hq must be a multiple of Hkv";
         case FA_ERR_HEADDIM: return "unsupported head size d (supported: 64, 128)";
         case FA_ERR_ARG: return "invalid scalar argument (scale must be finite, num_splits in 1..256, p_drop in [0, 1))";
-        case FA_ERR_WORKSPACE: return "workspace is null or smaller than the size the entry point needs";
+        case FA_ERR_WORKSPACE: return "workspace is null, not 16-byte aligned or smaller than the size the entry point needs";
         case FA_ERR_HIP: return "HIP launch failed";
         default: return "unknown status";
     }

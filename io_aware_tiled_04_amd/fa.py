@@ -166,27 +166,36 @@ def fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse
 
     q [B,Hq,N,d], k/v [B,Hkv,N,d]: contiguous bf16 (or fp32) device tensors.
     O has q's dtype and shape; LSE is fp32 [B,Hq,N].  ``scale`` defaults to
-    1/sqrt(d).  Launches on ``stream`` (a torch stream) or torch's current
-    stream, without synchronising.
+    1/sqrt(d).  ``out`` and ``lse_out``, when given, must have exactly those
+    shapes (the kernel writes B*Hq*N*d and B*Hq*N elements); every shape is
+    checked before anything is launched.  Launches on ``stream`` (a torch
+    stream) or torch's current stream, without synchronising.
     """
     import torch
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        if not isinstance(t, torch.Tensor) or t.dim() != 4:
+            raise ValueError(f"{n} must be a 4-D [B, H, N, d] torch.Tensor")
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    if tuple(k.shape) != (B, Hkv, N, d) or tuple(v.shape) != (B, Hkv, N, d):
+        raise ValueError("k and v must be [B, Hkv, N, d] with q's B, N and d")
+    if out is not None and (not isinstance(out, torch.Tensor) or tuple(out.shape) != tuple(q.shape)):
+        raise ValueError(f"out must have q's shape {tuple(q.shape)}")
+    if lse_out is not None and (not isinstance(lse_out, torch.Tensor) or tuple(lse_out.shape) != (B, Hq, N)):
+        raise ValueError(f"lse_out must have shape {(B, Hq, N)}")
     dev = q.device
     dtype = q.dtype
     if dtype not in (torch.bfloat16, torch.float32):
         raise TypeError("q must be bfloat16 or float32")
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _check(t, n, dtype, dev)
-    B, Hq, N, d = q.shape
-    Hkv = k.shape[1]
-    if tuple(k.shape) != (B, Hkv, N, d) or tuple(v.shape) != (B, Hkv, N, d):
-        raise ValueError("k and v must be [B, Hkv, N, d] with q's B, N and d")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     o = torch.empty_like(q) if out is None else out
     lse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev) if lse_out is None else lse_out
     _check(o, "out", dtype, dev)
-    if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != (B, Hq, N):
-        raise ValueError("lse_out must be a contiguous fp32 [B, Hq, N] tensor")
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or lse.device != dev:
+        raise ValueError("lse_out must be a contiguous fp32 tensor on q's device")
     s = (stream if stream is not None else torch.cuda.current_stream(dev)).cuda_stream
     fn = fa_fwd if dtype == torch.bfloat16 else fa_fwd_f32
     rc = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
@@ -222,6 +231,8 @@ def fwd_splitkv(q, k, v, num_splits: int, causal: bool = False, scale: float | N
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     if workspace.device != dev or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous tensor on q's device")
+    if workspace.data_ptr() % 16 != 0:
+        raise ValueError("workspace must start at a 16-byte aligned address")
     o = torch.empty_like(q)
     lse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
     s = (stream if stream is not None else torch.cuda.current_stream(dev)).cuda_stream

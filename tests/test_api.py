@@ -99,6 +99,9 @@ def test_splitkv_rejects_the_common_invalid_arguments():
     (2, P, 0, "FA_ERR_WORKSPACE"),
     # 2 splits of [1, 4, 300, 64]: 2 * 4 * 300 * 65 * 4 bytes, one byte short
     (2, P, 2 * 4 * 300 * 65 * 4 - 1, "FA_ERR_WORKSPACE"),
+    # the split kernels store float4 values: the workspace must be 16-byte aligned
+    (2, P + 8, 1 << 30, "FA_ERR_WORKSPACE"),
+    (2, P + 4, 1 << 30, "FA_ERR_WORKSPACE"),
 ])
 def test_splitkv_checks_splits_and_workspace(splits, ws, wbytes, expect):
     from io_aware_tiled_04_amd import fa
@@ -241,3 +244,22 @@ def test_workloads_are_seeded_and_shaped():
     assert 1.8 < q.float().std().item() < 2.2 and 0.9 < v.float().std().item() < 1.1
     assert CONFIGS["c1"].dtype == "f32" and make_inputs(CONFIGS["c1"])[0].dtype == torch.float32
     assert CONFIGS["c3"].nominal_flops() == 4 * 2 * 32 * 4096 ** 2 * 128 / 2
+
+
+@pytest.mark.parametrize("bad", ["out", "lse_out"])
+def test_fwd_rejects_wrong_output_shapes_before_any_launch(bad):
+    """A caller-supplied output of the wrong shape is rejected in the binding
+    before anything reaches the library (the kernel writes B*Hq*N*d outputs
+    and B*Hq*N logsumexps; a smaller buffer would be written past its end).
+    The check comes before the device checks, so it holds on CPU tensors."""
+    import torch
+    from io_aware_tiled_04_amd import fa
+    q = torch.zeros(1, 4, 64, 128, dtype=torch.bfloat16)
+    k = torch.zeros(1, 2, 64, 128, dtype=torch.bfloat16)
+    kw = {"out": torch.zeros(1, 4, 63, 128, dtype=torch.bfloat16)} if bad == "out" else \
+        {"lse_out": torch.zeros(1, 4, 32, dtype=torch.float32)}
+    with pytest.raises(ValueError, match=bad):
+        fa.fwd(q, k, k, causal=True, **kw)
+    # right shapes pass the shape checks and stop at the device check instead
+    with pytest.raises(ValueError, match="GPU"):
+        fa.fwd(q, k, k, causal=True, out=torch.zeros_like(q))

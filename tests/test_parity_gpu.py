@@ -4,9 +4,11 @@ Tolerances (absolute, over every compared element):
   bf16 inputs: max |dO| <= 2e-2 and mean |dO| <= 2e-3;
   fp32 inputs: max |dO| <= 1e-5;
   all: max |dLSE| <= 1e-3.
-Reduced sizes are compared element by element against the full oracle; the
-full-size configurations are compared on sampled query rows (the oracle row by
-row) and checked on every element through closed forms.
+Reduced sizes are compared element by element against the full oracle.  The
+full-size configurations are compared on every element of O and LSE against
+the oracle evaluated block of rows by block of rows (the same definition:
+a row of O depends only on its own query row), on sampled rows, and through
+closed forms.
 """
 import math
 
@@ -76,10 +78,9 @@ SMALL = [
     # 32 and 64 query heads: the XCD work order that takes heads four at a time
     Workload("h32-gqa-ragged", 1, 32, 8, 300, 64, True, "bf16", 72),
     Workload("h64-noncausal-ragged", 2, 32, 32, 130, 128, False, "bf16", 73),
-    # More query tiles than compute units: resident workgroups that walk
-    # several items each, with the next item's Q rows and first K tile loaded
-    # during the current one.  One case per head-count branch of the work
-    # order (multiple of 32, multiple of 8, neither), ragged tails, GQA.
+    # Many more query tiles than compute units, one case per branch of the
+    # work order (head count a multiple of 32, a multiple of 8, neither),
+    # with ragged tails and GQA.
     Workload("resident-h64-gqa-ragged", 1, 64, 16, 1100, 128, True, "bf16", 74),
     Workload("resident-h72-gqa-ragged", 3, 24, 6, 1100, 128, True, "bf16", 75),
     Workload("resident-h37-d64-ragged", 1, 37, 37, 2000, 64, True, "bf16", 76),
@@ -120,6 +121,48 @@ def test_parity_full_size_sampled_rows(name):
     mx, mean, lmx = _check(w, o[idx], lse[idx], o_ref, lse_ref)
     _say(f"{name} sampled {len(rows)} rows: max|dO|={mx:.3e} mean|dO|={mean:.3e} "
          f"max|dLSE|={lmx:.3e}")
+
+
+def _oracle_full_in_row_blocks(w, q, k, v, rows_per_block=1024, workers=16):
+    """The oracle's O and LSE for every row of every head, computed block of
+    query rows by block of query rows (each block against the head's full key
+    set, exactly as oracle.attention_ref does for the whole head), spread
+    over a thread pool with single-threaded BLAS.  This bounds host memory
+    at the long configurations (one block's S and P instead of N x N)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    from threadpoolctl import threadpool_limits
+
+    B, Hq, N, _ = q.shape
+    o_ref = np.empty(q.shape, dtype=np.float64)
+    lse_ref = np.empty((B, Hq, N), dtype=np.float64)
+    jobs = [(b, h, r0) for b in range(B) for h in range(Hq) for r0 in range(0, N, rows_per_block)]
+
+    def one(job):
+        b, h, r0 = job
+        r1 = min(N, r0 + rows_per_block)
+        hk = oracle.kv_head(h, Hq, k.shape[1])
+        o_ref[b, h, r0:r1], lse_ref[b, h, r0:r1] = oracle.attention_head(
+            q[b, h, r0:r1], k[b, hk], v[b, hk], w.scale, w.causal, row_index=np.arange(r0, r1))
+
+    with threadpool_limits(1), ThreadPoolExecutor(max_workers=workers) as ex:
+        list(ex.map(one, jobs))
+    return o_ref, lse_ref
+
+
+@pytest.mark.parametrize("name", ["c3", "c4", "c5"])
+def test_parity_full_size_every_element(name):
+    """Full configuration on its seeded inputs, launched exactly as the bench
+    launches it: every element of O and LSE against the fp64 oracle, with the
+    tolerances taken over all elements (max and mean |dO|, max |dLSE|)."""
+    import time
+    w = CONFIGS[name]
+    q, k, v, o, lse = _run(w)
+    t0 = time.perf_counter()
+    o_ref, lse_ref = _oracle_full_in_row_blocks(w, q, k, v)
+    mx, mean, lmx = _check(w, o, lse, o_ref, lse_ref)
+    _say(f"{name} every element ({o.size} O, {lse.size} LSE; oracle {time.perf_counter() - t0:.1f} s): "
+         f"max|dO|={mx:.3e} mean|dO|={mean:.3e} max|dLSE|={lmx:.3e}")
 
 
 LONG = [
