@@ -76,9 +76,9 @@ enum fa_status {
  *   logsumexp of the scaled, masked scores of each query row.
  * d in {64, 128}; N >= 1 (any length; partial tiles are masked).
  * Products Q K^T and P V run on bf16 matrix cores with fp32 accumulation; the
- * softmax state (row max, row sum, output accumulator) is fp32.  The row sum
- * is taken over the fp32 probabilities before they are rounded to bf16 for
- * the P V product.
+ * softmax state (row max, row sums, output accumulator) is fp32.  The
+ * logsumexp takes the row sum of the fp32 weights; O is divided by the row
+ * sum of the same weights rounded to bf16, the values that enter P V.
  * Returns FA_OK or a negative fa_status.
  */
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,

@@ -18,6 +18,12 @@
 // Polish notes (section "Nie wystarczy uśrednić wyników bloków": keep m, l and
 // u, divide u by l at the end).  The epilogue divides by l and writes the
 // natural-log logsumexp m + ln l that the blog's backward section keeps.
+// Two row sums are kept: l over the fp32 weights (for the logsumexp) and l~
+// over the bf16-rounded weights that actually enter P V, formed on the
+// matrix cores beside P V; O is divided by l~, so that it is exactly the
+// weighted mean the matrix cores accumulated.  (Dividing by l instead adds
+// the rounding error of the largest weight, up to 2^-9 |v|, to every row a
+// single key dominates.)
 //
 // Scheduling choices (the arithmetic is that of the method):
 //  * Ping-pong.  The 8 waves form two groups with one wave of each on every
@@ -68,6 +74,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 #define LDS __attribute__((address_space(3)))
@@ -191,6 +198,24 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// Row sum of the rounded weights on the matrix cores.  The P operand pb[c]
+// of a 16-key chunk (lane l: query l % 32, 8 of the chunk's keys) read as
+// the B operand of a 16x16x32 product is B[k][n] with n = l % 16 and k in
+// the 8-block l / 16.  The A operand `ones_pattern` has ones exactly where
+// ((m >> 2) & 1) == (k-block & 1) (lane l holds row m = l % 16 of k-block
+// l / 16), so output row m sums, for column n, the 16 keys of query n (m in
+// 0..3, 8..11) or of query n + 16 (m in 4..7, 12..15).  The accumulator
+// layout (lane l: rows 4 (l / 16) .. +3 of column l % 16) then gives every
+// lane four copies of the chunk's sum for its own query l % 32.
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ bf16x8 ones_pattern(int lane) {
+    const bool one = (((lane & 15) >> 2) & 1) == ((lane >> 4) & 1);
+    const uint32_t w = one ? 0x3F803F80u : 0u;    // two bf16 ones, or zeros
+    return __builtin_bit_cast(bf16x8, (u32x4){w, w, w, w});
+}
+
 // Lane l and lane l^32 hold the same query: after the swap, out[0] and out[1]
 // are x[l] and x[l^32] in some order, in every lane.
 __device__ __forceinline__ float half_swap_sum(float x) {
@@ -272,16 +297,20 @@ struct MaskTag {
 constexpr int kSchedMfma = 0x008;
 constexpr int kSchedDsRead = 0x100;
 
-template <int D, bool HAS_PV, bool HAS_S>
+template <int D, bool HAS_PV, bool HAS_S, bool LT>
 __device__ __forceinline__ void gemm_phase(const LDS char* vl, const LDS char* kl,
                                            const bf16x8 (&pb)[Tile<D>::BC / 16],
                                            const bf16x8 (&qf)[D / 16], f32x16 (&oacc)[D / 32],
-                                           f32x16 (&s)[Tile<D>::KB], int lane) {
+                                           f32x16 (&s)[Tile<D>::KB], f32x4& lt, bf16x8 ones, int lane) {
     using T = Tile<D>;
     constexpr int DB = D / 32;
     constexpr int NPV = HAS_PV ? (T::BC / 16) * DB : 0;
     constexpr int NS = HAS_S ? (D / 16) * T::KB : 0;
     constexpr int NF = NPV + NS;
+    // LT: the row sum of the rounded weights of the previous tile, one small
+    // product per 16-key chunk; they need no LDS operand, so they go first,
+    // while the first operand reads are in flight.
+    constexpr int NLT = (HAS_PV && LT) ? T::BC / 16 : 0;
     // Operands 0 .. NS-1 are those of S^T = K Q^T, then those of the P V
     // product: the S accumulators are complete first, so the wave's next
     // (vector) phase can start on them while the P V MFMAs drain.
@@ -311,6 +340,8 @@ __device__ __forceinline__ void gemm_phase(const LDS char* vl, const LDS char* k
         for (int kb = 0; kb < T::KB; ++kb) s[kb] = (f32x16){};
     }
 #pragma unroll
+    for (int c = 0; c < NLT; ++c) lt = mfma16(ones, pb[c], lt);
+#pragma unroll
     for (int i = 0; i < NF; ++i) {
         if (i >= NS) {
             const int j = i - NS;
@@ -325,6 +356,7 @@ __device__ __forceinline__ void gemm_phase(const LDS char* vl, const LDS char* k
     if constexpr (NF > kAhead) {
         constexpr int first_reads = NS >= kAhead ? kAhead : NS + 2 * (kAhead - NS);
         __builtin_amdgcn_sched_group_barrier(kSchedDsRead, first_reads, 0);
+        if constexpr (NLT > 0) __builtin_amdgcn_sched_group_barrier(kSchedMfma, NLT, 0);
 #pragma unroll
         for (int i = 0; i < NF - kAhead; ++i) {
             __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
@@ -391,7 +423,7 @@ __device__ __forceinline__ void apply_dropout(bf16x8 (&pb)[Tile<D>::BC / 16], in
 // reference gives the same O = sum p v / sum p and LSE = m + log2 l.
 template <int D, bool CAUSAL, bool MASK>
 __device__ __forceinline__ void softmax_tile(f32x16 (&s)[Tile<D>::KB], bf16x8 (&pb)[Tile<D>::BC / 16],
-                                             f32x16 (&oacc)[D / 32], float& m_run, float& l_run,
+                                             f32x16 (&oacc)[D / 32], f32x4& lt, float& m_run, float& l_run,
                                              int key0, int N, int my_row, float c_log2, int lane,
                                              bool first) {
     using T = Tile<D>;
@@ -436,6 +468,7 @@ __device__ __forceinline__ void softmax_tile(f32x16 (&s)[Tile<D>::KB], bf16x8 (&
     const float m_use = (m_new == -__builtin_inff()) ? 0.f : m_new;
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);   // 1 where the max stayed
     l_run *= alpha;
+    lt *= alpha;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
     m_run = m_use;
@@ -581,6 +614,13 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
 #pragma unroll
     for (int db = 0; db < DB; ++db) oacc[db] = (f32x16){};
     float m_run = -__builtin_inff();   // reference max of S*c (log2 domain)
+    // Row sum of the bf16-rounded weights that enter P V (the same value in
+    // all four registers): O is divided by it, so that O is exactly the
+    // weighted mean the matrix cores formed, while l_run (fp32 weights)
+    // gives the logsumexp.  With dropout the matrix phase sees the thinned
+    // weights, so that path keeps l_run for both.
+    f32x4 lt = (f32x4){};
+    const bf16x8 ones = ones_pattern(lane);
     float l_run = 0.f;                 // this lane's share of the running sum
     f32x16 s[KB];
     bf16x8 pb[BC / 16];
@@ -626,11 +666,11 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
         // issue priority keeps the MFMAs from waiting behind it.
         __builtin_amdgcn_s_setprio(kMatrixPrio);
         if (has_pv && has_s)
-            gemm_phase<D, true, true>(vl, kl, pb, qf, oacc, s, lane);
+            gemm_phase<D, true, true, !DROP>(vl, kl, pb, qf, oacc, s, lt, ones, lane);
         else if (has_pv)
-            gemm_phase<D, true, false>(vl, kl, pb, qf, oacc, s, lane);
+            gemm_phase<D, true, false, !DROP>(vl, kl, pb, qf, oacc, s, lt, ones, lane);
         else if (has_s)
-            gemm_phase<D, false, true>(vl, kl, pb, qf, oacc, s, lane);
+            gemm_phase<D, false, true, !DROP>(vl, kl, pb, qf, oacc, s, lt, ones, lane);
         __builtin_amdgcn_s_setprio(0);
     };
     // MASKED: the tile may hold dead keys (past N, or after some query of
@@ -638,7 +678,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     auto softmax_phase = [&](auto masked, int t) __attribute__((always_inline)) {
         if (t >= 0 && t < w_tiles) {
             const int key0 = (kt_lo + t) * BC;
-            softmax_tile<D, CAUSAL, decltype(masked)::value>(s, pb, oacc, m_run, l_run, key0, N, my_row,
+            softmax_tile<D, CAUSAL, decltype(masked)::value>(s, pb, oacc, lt, m_run, l_run, key0, N, my_row,
                                                              c_log2, lane, t == 0);
             // Dropout thins the weights that enter P V; the row sum above
             // took them whole.
@@ -683,7 +723,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     if constexpr (SPLIT) {
         if (my_row >= N) return;
         const bool seen = l_tot > 0.f;       // the row saw some key of the range
-        const float inv = seen ? 1.f / l_tot : 0.f;
+        // (a row that sees a key has its largest weight at 1 in the tile that
+        // set its reference, so the rounded sum is at least 1)
+        const float inv = seen ? 1.f / lt[0] : 0.f;
         const size_t prow = ((size_t)split * bh_total + bh) * N + my_row;
         float* opp = OP + prow * D;
 #pragma unroll
@@ -707,7 +749,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     constexpr int RC = D / 8;                        // 16-byte chunks per row
     constexpr int RPI = 1024 / (2 * D);              // rows per store instruction
     static_assert(kWaves * kWaveRows * 2 * D <= T::VBASE + T::NBUF * T::VBYTES, "O staging fits the rings");
-    const float inv = DROP ? dr.factor / l_tot : 1.f / l_tot;
+    const float inv = DROP ? dr.factor / l_tot : 1.f / lt[0];
     LDS char* ot = smem + wave * (kWaveRows * 2 * D);
     // (the per-lane swizzle keys are hidden from the optimiser, which would
     // otherwise precompute all 24 addresses and keep them live from the start)

@@ -221,15 +221,18 @@ def test_first_causal_row_is_v0():
     assert np.max(np.abs(lse[:, :, 0] - ref)) <= TOL_LSE
 
 
-@pytest.mark.parametrize("slope", [0.5, -0.5])
+@pytest.mark.parametrize("slope", [0.5, -0.5, 2.0])
 @pytest.mark.parametrize("causal", [True, False])
 def test_logits_that_move_every_tile(slope, causal):
-    """Scaled logits that rise (or fall) by 0.5 per key.  Rising, every
-    64-key tile's max exceeds the reference of the tiles before by about 46
-    in log2 units, so every tile takes the exact-max redo with a rescale of O
-    and l; falling, the first tile's reference holds and the later weights
-    underflow to zero.  Q is zero but for one column of ones (exact in
-    bf16), so the logits come from that column of K alone."""
+    """Scaled logits that rise (or fall) by `slope` per key.  Rising by 0.5,
+    every 64-key tile's max exceeds the reference of the tiles before by
+    about 46 in log2 units, so every tile moves the reference (with finite
+    weights above the row-sum limit) and rescales O and l; rising by 2, the
+    weights against the old reference overflow fp32 in every tile, so every
+    tile takes the exact row max from S recomputed; falling, the first
+    tile's reference holds and the later weights underflow to zero.  Q is
+    zero but for one column of ones (exact in bf16), so the logits come from
+    that column of K alone."""
     w = Workload("moving-max", 1, 2, 1, 1000, 128, causal, "bf16", 85)
     g = torch.Generator().manual_seed(85)
     q = torch.zeros(w.B, w.Hq, w.N, w.d)
