@@ -63,8 +63,12 @@ enum fa_status {
     FA_ERR_HEADDIM = -4,   /* d is not one of the supported head sizes (64, 128) */
     FA_ERR_ARG = -5,       /* scale is not finite, num_splits or p_drop is out of range */
     FA_ERR_HIP = -6,       /* the HIP runtime rejected the launch */
-    FA_ERR_WORKSPACE = -7  /* a workspace argument is null, misaligned or too small */
+    FA_ERR_WORKSPACE = -7, /* a workspace argument is null, misaligned or too small */
+    FA_ERR_SCRATCH = -8    /* the problem needs more than the fixed scratch of fa_fwd_splitkv_noalloc */
 };
+
+/* Bytes of the fixed device scratch array of fa_fwd_splitkv_noalloc (64 MiB). */
+#define FA_NOALLOC_SCRATCH_BYTES (64u << 20)
 
 /*
  * fa_fwd - attention forward pass on bfloat16 inputs (the hot path).
@@ -134,6 +138,38 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
                    int B, int Hq, int Hkv, int N, int d, int causal, float scale,
                    int num_splits, void* workspace, size_t workspace_bytes,
                    hipStream_t stream);
+
+/*
+ * fa_fwd_splitkv_noalloc - fa_fwd_splitkv without a workspace argument and
+ * without any allocation, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).
+ *
+ * The split partials go to a fixed device array inside the library of
+ * FA_NOALLOC_SCRATCH_BYTES bytes (64 MiB).  Each GPU the entry point runs on
+ * gets its own copy on the first call there (the library looks up its
+ * address once per device; that first call loads the array) and keeps it
+ * until the process ends.  The call itself allocates and frees nothing.
+ *
+ * Arguments: as for fa_fwd_splitkv without workspace and workspace_bytes;
+ * the result is fa_fwd_splitkv's, bit for bit, for the same num_splits.
+ * Limit: fa_fwd_splitkv_workspace_size(B, Hq, N, d, num_splits) must not
+ * exceed FA_NOALLOC_SCRATCH_BYTES; larger problems return FA_ERR_SCRATCH
+ * before any HIP call (use fewer splits, or fa_fwd_splitkv with a caller
+ * workspace).
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents: calls that overlap in time on one GPU (two streams, two host
+ * threads) race on it and may give wrong results.  Calls on one stream, or
+ * otherwise ordered, are safe.  Nothing in the array needs to be cleared
+ * between calls: the first kernel writes every partial the merge reads.
+ * Returns FA_OK or a negative fa_status (FA_ERR_ARG for num_splits,
+ * FA_ERR_SCRATCH for a problem too large for the array, FA_ERR_HIP if the
+ * array's address cannot be obtained or a launch fails, otherwise as
+ * fa_fwd).
+ */
+int fa_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                           int num_splits, hipStream_t stream);
 
 /*
  * fa_fwd_dropout - fa_fwd with dropout on the attention weights.

@@ -136,6 +136,26 @@ extern "C" int fa_fwd_splitkv(const void* q, const void* k, const void* v, void*
     return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+extern "C" int fa_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                                      int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                                      int num_splits, hipStream_t stream) {
+    int rc = validate(q, k, v, o, lse, B, Hq, Hkv, N, d, scale);
+    if (rc != FA_OK) return rc;
+    if (num_splits < 1 || num_splits > fa::kMaxSplits) return FA_ERR_ARG;
+    const long long need = fa::split_workspace_floats(B, Hq, N, d, num_splits) * 4;
+    if (need > (long long)FA_NOALLOC_SCRATCH_BYTES) return FA_ERR_SCRATCH;
+    // the split checks proper, with the scratch standing in for a workspace
+    // (its address is 256-byte aligned, so a stand-in with that alignment
+    // is checked here, before any HIP call)
+    rc = validate_split(B, Hq, N, d, num_splits, (const void*)(uintptr_t)256, FA_NOALLOC_SCRATCH_BYTES);
+    if (rc != FA_OK) return rc;
+    float* ws = nullptr;
+    if (fa::noalloc_scratch(&ws) != hipSuccess) return FA_ERR_HIP;
+    const hipError_t e = fa::launch_fwd_bf16_split(pack(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale),
+                                                   num_splits, ws, stream);
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 extern "C" size_t fa_fwd_kvouter_workspace_size(int B, int Hq, int N, int d) {
     if (B <= 0 || Hq <= 0 || N <= 0 || (d != 64 && d != 128)) return 0;
     if ((double)B * Hq * (double)N * 128.0 >= 1125899906842624.0) return 0;
@@ -242,6 +262,7 @@ extern "C" const char* fa_status_string(int status) {
         case FA_ERR_HEADDIM: return "unsupported head size d (supported: 64, 128)";
         case FA_ERR_ARG: return "invalid scalar argument (scale must be finite, num_splits in 1..256, p_drop in [0, 1))";
         case FA_ERR_WORKSPACE: return "workspace is null, not 16-byte aligned or smaller than the size the entry point needs";
+        case FA_ERR_SCRATCH: return "problem needs more than the 64 MiB fixed scratch of fa_fwd_splitkv_noalloc (use fewer splits or a workspace)";
         case FA_ERR_HIP: return "HIP launch failed";
         default: return "unknown status";
     }

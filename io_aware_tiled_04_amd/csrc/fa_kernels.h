@@ -59,6 +59,10 @@ hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
 // kvouter_workspace_floats(...) elements).
 hipError_t launch_fwd_bf16_kvouter(const FwdArgs& a, float* workspace, hipStream_t stream);
 long long kvouter_workspace_floats(long long B, long long Hq, long long N, long long d);
+// Device address of the current device's fixed scratch array of the
+// allocation-free split-KV entry point (FA_NOALLOC_SCRATCH_BYTES bytes),
+// looked up on the first call on each device.
+hipError_t noalloc_scratch(float** out);
 // Backward pass: D = rowsum(dO * O) into `workspace` (B*Hq*N floats), then
 // the dQ, dK and dV kernels, all enqueued on `stream`.
 hipError_t launch_bwd_bf16(const BwdArgs& a, float* workspace, hipStream_t stream);

@@ -27,10 +27,14 @@ FA_ERR_HEADDIM = -4
 FA_ERR_ARG = -5
 FA_ERR_HIP = -6
 FA_ERR_WORKSPACE = -7
+FA_ERR_SCRATCH = -8
+
+# Bytes of the fixed device scratch array of fa_fwd_splitkv_noalloc.
+FA_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 # Names declared in include/fa.h, in order.
 EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_fwd_splitkv_workspace_size", "fa_fwd_splitkv",
-           "fa_fwd_dropout", "fa_fwd_kvouter_workspace_size", "fa_fwd_kvouter", "fa_bwd_workspace_size",
+           "fa_fwd_splitkv_noalloc", "fa_fwd_dropout", "fa_fwd_kvouter_workspace_size", "fa_fwd_kvouter", "fa_bwd_workspace_size",
            "fa_bwd", "fa_bwd_dropout", "fa_status_string")
 
 
@@ -48,6 +52,8 @@ def _load():
     lib.fa_fwd_splitkv.argtypes = fwd_args[:-1] + [ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t,
                                                    ctypes.c_void_p]
     lib.fa_fwd_splitkv.restype = ctypes.c_int
+    lib.fa_fwd_splitkv_noalloc.argtypes = fwd_args[:-1] + [ctypes.c_int, ctypes.c_void_p]
+    lib.fa_fwd_splitkv_noalloc.restype = ctypes.c_int
     lib.fa_fwd_dropout.argtypes = fwd_args[:-1] + [ctypes.c_float, ctypes.c_ulonglong, ctypes.c_uint,
                                                    ctypes.c_void_p]
     lib.fa_fwd_dropout.restype = ctypes.c_int
@@ -104,6 +110,14 @@ def fa_fwd_splitkv(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, num_splits,
     """Raw call of the split-KV C entry point; pointers and stream are integers."""
     return _lib.fa_fwd_splitkv(q, k, v, o, lse, B, Hq, Hkv, N, d, int(causal), float(scale),
                                int(num_splits), workspace, int(workspace_bytes), stream)
+
+
+def fa_fwd_splitkv_noalloc(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, num_splits, stream) -> int:
+    """Raw call of the allocation-free split-KV C entry point (partials in the
+    library's fixed per-device scratch array); pointers and stream are
+    integers."""
+    return _lib.fa_fwd_splitkv_noalloc(q, k, v, o, lse, B, Hq, Hkv, N, d, int(causal), float(scale),
+                                       int(num_splits), stream)
 
 
 def fa_fwd_dropout(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, p_drop, seed, offset,

@@ -21,7 +21,7 @@ def _declared():
 
 def test_header_declares_the_entry_points():
     assert _declared() == ["fa_fwd", "fa_fwd_f32", "fa_fwd_splitkv_workspace_size",
-                           "fa_fwd_splitkv", "fa_fwd_dropout", "fa_fwd_kvouter_workspace_size",
+                           "fa_fwd_splitkv", "fa_fwd_splitkv_noalloc", "fa_fwd_dropout", "fa_fwd_kvouter_workspace_size",
                            "fa_fwd_kvouter", "fa_bwd_workspace_size", "fa_bwd", "fa_bwd_dropout",
                            "fa_status_string"]
 
@@ -263,3 +263,26 @@ def test_fwd_rejects_wrong_output_shapes_before_any_launch(bad):
     # right shapes pass the shape checks and stop at the device check instead
     with pytest.raises(ValueError, match="GPU"):
         fa.fwd(q, k, k, causal=True, out=torch.zeros_like(q))
+
+
+def test_noalloc_splitkv_rejects_before_any_hip_call():
+    """The allocation-free split-KV entry point runs the common validation,
+    checks the split count, and rejects a problem whose partials exceed the
+    fixed scratch array (FA_ERR_SCRATCH), all before any HIP call."""
+    from io_aware_tiled_04_amd import fa
+    cases = [
+        ((0, P, P, P, P, 1, 1, 1, 128, 64, 0, 0.125), 2, "FA_ERR_NULL"),
+        ((P, P, P, P, P, 1, 6, 4, 128, 64, 1, 0.125), 2, "FA_ERR_HEADS"),
+        ((P, P, P, P, P, 1, 1, 1, 128, 80, 1, 0.125), 2, "FA_ERR_HEADDIM"),
+        ((P, P, P, P, P, 1, 1, 1, 128, 64, 1, math.nan), 2, "FA_ERR_ARG"),
+        ((P, P, P, P, P, 1, 1, 1, 128, 64, 1, 0.125), 0, "FA_ERR_ARG"),
+        ((P, P, P, P, P, 1, 1, 1, 128, 64, 1, 0.125), 257, "FA_ERR_ARG"),
+        # 4 splits of [1, 4, 16384, 128]: 4 * 4 * 16384 * 129 * 4 bytes > 64 MiB
+        ((P, P, P, P, P, 1, 4, 4, 16384, 128, 1, 0.125), 4, "FA_ERR_SCRATCH"),
+        # the largest problem at 1 split that fits: B*Hq*N*(d+1)*4 <= 64 MiB
+        ((P, P, P, P, P, 1, 1, 1, (64 << 20) // (129 * 4) + 1, 128, 1, 0.125), 1, "FA_ERR_SCRATCH"),
+    ]
+    for args, splits, expect in cases:
+        rc = fa.fa_fwd_splitkv_noalloc(*args, splits, 0)
+        assert rc == getattr(fa, expect), (args, splits, rc, fa.fa_status_string(rc))
+    assert fa.fa_fwd_splitkv_workspace_size(1, 4, 16384, 128, 4) > fa.FA_NOALLOC_SCRATCH_BYTES
