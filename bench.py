@@ -36,7 +36,7 @@ sys.path.insert(0, ROOT)
 METRIC = "attention fwd TFLOP/s (bf16, causal, N=4096 d=128) + % of MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 KERNEL_SRC = os.path.join(ROOT, "io_aware_tiled_04_amd", "csrc", "fa_fwd_bf16.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_bf16_c3_hbm_traffic.md")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_bf16_c3_trace_and_counters.md")
 COPY_BYTES = 512 << 20
 
 
@@ -118,84 +118,56 @@ def cpu_model() -> str | None:
     return None
 
 
-class ClockSampler:
-    """Samples the GPU's shader (gfx) clock in a background thread while the
-    timed launches run, through the AMD SMI library's metrics table (or the
-    sysfs DPM table when that is not available).  Reads only: it changes no
-    clock or power setting.  ``mhz`` is None when no source is readable."""
+CLOCK_LIB = os.path.join(ROOT, "io_aware_tiled_04_amd", "libfa_clock.so")
 
-    def __init__(self, period_s: float = 0.002):
-        import threading
-        self.period = period_s
-        self.samples = []
-        self.source = None
-        self._stop = threading.Event()
-        self._thread = None
-        self._read = self._pick_source()
 
-    def _pick_source(self):
-        try:
-            import amdsmi
-            amdsmi.amdsmi_init()
-            handle = amdsmi.amdsmi_get_processor_handles()[0]
+class ClockProbe:
+    """The shader clock under load: a one-wave probe kernel (libfa_clock.so)
+    on a second stream, at the default priority, spins for a fixed window of
+    the GPU's constant-rate real-time counter while the timed launches run
+    and counts the shader-clock cycles that pass.  clock = cycles / window,
+    with the window timed by HIP events on the probe's stream.  The window
+    is made shorter than the timed region so that the probe sees only the
+    attention kernel's load.  ``mhz`` is None when the probe library is
+    missing or the window could not be timed."""
 
-            def read_smi():
-                m = amdsmi.amdsmi_get_gpu_metrics_info(handle)
-                for key in ("current_gfxclk", "average_gfxclk_frequency"):
-                    v = m.get(key)
-                    if isinstance(v, (int, float)) and 0 < v < 10000:
-                        return float(v)
-                clks = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, (int, float))
-                        and 0 < c < 10000]
-                return sum(clks) / len(clks) if clks else None
+    def __init__(self, window_ms: float):
+        import ctypes
+        import torch
+        self.mhz = None
+        self.window_ms = window_ms
+        self._lib = None
+        if os.path.exists(CLOCK_LIB):
+            self._lib = ctypes.CDLL(CLOCK_LIB)
+            self._lib.fa_bench_clock_probe.argtypes = [ctypes.c_void_p, ctypes.c_ulonglong, ctypes.c_void_p]
+            self._lib.fa_bench_clock_probe.restype = ctypes.c_int
+        self._out = torch.zeros(2, dtype=torch.int64, device="cuda")
+        self._stream = torch.cuda.Stream()
+        self._e0 = torch.cuda.Event(enable_timing=True)
+        self._e1 = torch.cuda.Event(enable_timing=True)
 
-            if read_smi() is not None:
-                self.source = "amdsmi gpu_metrics"
-                return read_smi
-        except Exception:
-            pass
-        for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
-            def read_sysfs(path=path):
-                with open(path, encoding="utf-8") as f:
-                    for line in f:
-                        if line.rstrip().endswith("*"):
-                            return float(line.split(":")[1].strip().rstrip("*").strip().lower()
-                                         .replace("mhz", ""))
-                return None
-            try:
-                if read_sysfs() is not None:
-                    self.source = "sysfs pp_dpm_sclk"
-                    return read_sysfs
-            except Exception:
-                continue
-        return None
+    def start(self):
+        if self._lib is None:
+            return
+        # ticks of the 100 MHz real-time counter; the window is timed by
+        # events, so the counter's exact rate does not enter the result
+        ticks = int(self.window_ms * 1e5)
+        self._e0.record(self._stream)
+        rc = self._lib.fa_bench_clock_probe(self._out.data_ptr(), ticks, self._stream.cuda_stream)
+        self._e1.record(self._stream)
+        if rc != 0:
+            self._lib = None
 
-    def _loop(self):
-        while not self._stop.is_set():
-            try:
-                v = self._read()
-                if v is not None:
-                    self.samples.append(v)
-            except Exception:
-                pass
-            self._stop.wait(self.period)
-
-    def __enter__(self):
-        import threading
-        if self._read is not None:
-            self._thread = threading.Thread(target=self._loop, daemon=True)
-            self._thread.start()
-        return self
-
-    def __exit__(self, *exc):
-        self._stop.set()
-        if self._thread is not None:
-            self._thread.join()
-        return False
-
-    @property
-    def mhz(self):
-        return sum(self.samples) / len(self.samples) if self.samples else None
+    def finish(self):
+        import torch
+        if self._lib is None:
+            return
+        torch.cuda.synchronize()
+        cycles, rticks = (int(x) for x in self._out.tolist())
+        ms = self._e0.elapsed_time(self._e1)
+        if ms > 0 and cycles > 0:
+            self.mhz = cycles / (ms * 1e3)
+            self.realtime_mhz = rticks / (ms * 1e3)
 
 
 def summarize(d: str, skip: int = 0) -> None:
@@ -304,25 +276,33 @@ def main() -> int:
         if rc != fa.FA_OK:
             raise fa.FaError(rc)
 
+    w0 = torch.cuda.Event(enable_timing=True)
+    w1 = torch.cuda.Event(enable_timing=True)
+    w0.record(stream)
     for _ in range(args.warmup):
         launch()
+    w1.record(stream)
     torch.cuda.synchronize()
+    warm_ms = w0.elapsed_time(w1) / max(1, args.warmup)
+    # probe window: about 70% of the expected timed region, 0.5 .. 40 ms
+    clock = ClockProbe(min(40.0, max(0.5, 0.7 * warm_ms * args.steps)))
 
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     region0 = torch.cuda.Event(enable_timing=True)
     region1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    with ClockSampler() as clock:
-        wall0 = time.perf_counter()
-        region0.record(stream)
-        for i in range(args.steps):
-            starts[i].record(stream)
-            launch()
-            ends[i].record(stream)
-        region1.record(stream)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - wall0
+    clock.start()
+    wall0 = time.perf_counter()
+    region0.record(stream)
+    for i in range(args.steps):
+        starts[i].record(stream)
+        launch()
+        ends[i].record(stream)
+    region1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    clock.finish()
     total_ms = region0.elapsed_time(region1)
     launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     avg_launch_ms = sum(launch_ms) / len(launch_ms)
@@ -385,8 +365,8 @@ def main() -> int:
                      "last5_launch_us": round(last_us, 2),
                      "last5_tflops": round(flops / (last_us * 1e-6) / 1e12, 2),
                      "sclk_mhz": round(clk, 1) if clk else None,
-                     "sclk_source": clock.source,
-                     "sclk_samples": len(clock.samples),
+                     "sclk_source": "s_memtime cycles of a one-wave probe on a second stream over "
+                                    f"{clock.window_ms:.1f} ms of the timed launches" if clk else None,
                      "peak_at_sclk": round(clock_peak, 1) if clock_peak else None,
                      "frac_at_sclk": round(achieved / clock_peak, 4) if clock_peak else None},
         "parity": {"rows": len(rows), "max_abs_o": float(err.max()),
@@ -718,6 +698,8 @@ def bench_backward(args) -> int:
             raise fa.FaError(rc)
 
     avg_ms, total_ms = _time_launches(launch, stream, args.steps, args.warmup)
+    if args.calibrate_copy:
+        _calibrate_copy(dev)
     # parity of the first GQA group of batch 0 (its query heads and its K/V
     # head) against the oracle's gradients; tolerances relative to each
     # gradient's magnitude, as in the backward tests

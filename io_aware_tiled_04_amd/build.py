@@ -1,8 +1,8 @@
 """Build the attention forward library (libfa.so) for gfx950 with hipcc.
 
 ``python -m io_aware_tiled_04_amd.build`` (or ``build()``) compiles every HIP
-source under ``csrc/`` and links ``libfa.so`` next to this file.  It always
-recompiles.  The library is loaded in-tree by ``io_aware_tiled_04_amd.fa``.
+source under ``csrc/`` and links ``libfa.so`` next to this file (and the
+bench's shader-clock probe into ``libfa_clock.so``).  It always recompiles.  The library is loaded in-tree by ``io_aware_tiled_04_amd.fa``.
 """
 from __future__ import annotations
 
@@ -48,8 +48,16 @@ def _run_all(cmds, verbose):
         raise RuntimeError(f"hipcc failed:\n{msg}")
 
 
+# The bench's shader-clock probe: a separate library, not part of the ABI.
+CLOCK_SRC = "clock_probe.hip"
+CLOCK_LIB = os.path.join(PKG, "libfa_clock.so")
+
+
 def build(verbose: bool = False, extra_flags=()) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
+    ctmp = CLOCK_LIB + ".tmp"
+    _run_all([[HIPCC, *FLAGS, "-shared", os.path.join(CSRC, CLOCK_SRC), "-o", ctmp]], verbose)
+    os.replace(ctmp, CLOCK_LIB)
     objs, cmds = [], []
     for src in SOURCES:
         obj = os.path.join(BUILD_DIR, src + ".o")
