@@ -465,7 +465,18 @@ def bench_splitkv(args) -> int:
     ok = bool(err.max() <= 2e-2 and err.mean() <= 2e-3 and lerr.max() <= 1e-3)
     flops = w.nominal_flops()
     rows_total = w.B * w.Hq * w.N
-    merge_bytes = S * rows_total * (w.d + 1) * 4 + rows_total * (2 * w.d + 4)
+    # The merge reads, for each row, the partials of the key ranges the row
+    # sees (all ranges with keys; when causal, those starting at or before
+    # the row), and writes O (bf16) and LSE once.
+    bc = 64 if w.d == 128 else 128                 # keys per tile of the kernel
+    n_kt = -(-w.N // bc)
+    kq, kr = divmod(n_kt, S)
+    starts = [(s * kq + min(s, kr)) * bc for s in range(S) if kq + (1 if s < kr else 0) > 0]
+    if w.causal:
+        seen = sum(sum(1 for st in starts if st <= r) for r in range(w.N))
+    else:
+        seen = len(starts) * w.N
+    merge_bytes = w.B * w.Hq * seen * (w.d + 1) * 4 + rows_total * (2 * w.d + 4)
     out = {
         "metric": "attention fwd TFLOP/s, split-KV path (bf16)",
         "value": round(flops * args.steps / (split_total * 1e-3) / 1e12, 2),

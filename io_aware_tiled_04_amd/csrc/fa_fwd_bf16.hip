@@ -484,7 +484,8 @@ __device__ __forceinline__ void softmax_tile(f32x16 (&s)[Tile<D>::KB], bf16x8 (&
 // tiles, then ranges of kq).  Without SPLIT, kq = T and kr = 0.  Each workgroup then writes the fp32 partial result
 // of its range instead of O and LSE: the output normalised by its own row
 // sum to OP[s][bh][row][d], and the logsumexp of its range to LP[s][bh][row]
-// (O = 0 and LSE = -inf for a row that sees no key of the range).
+// (O = 0 and LSE = -inf for a row of the tile that sees no key of the
+// range).  A workgroup whose tile sees no key of its range writes nothing.
 //
 // DROP (never with SPLIT): dropout with the parameters `dr` on the weights
 // that enter P V; the row sums, hence the logsumexp, take the weights whole,
@@ -637,19 +638,11 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     //   V_u, over V_{u-2} (read in phases 2u-2 and 2u-1), while that phase
     //   reads V_{u-1} from the other buffer, and waits for it at the end of
     //   its vector phase 2u+1; it is first read in phase 2u+2.
-    if (SPLIT && n_tiles == 0) {               // no key of the range is visible to the tile
-        if (my_row < N && wq0 < N) {
-            const size_t prow = ((size_t)split * bh_total + bh) * N + my_row;
-            float* opp = OP + prow * D;
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-#pragma unroll
-                for (int g = 0; g < 4; ++g)
-                    *(float4*)(opp + 32 * db + 8 * g + 4 * h) = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (h == 0) LP[prow] = -__builtin_inff();
-        }
-        return;
-    }
+    // No key of the range is visible to the tile: nothing to write (the
+    // merge takes split s for row r only when the range has keys and, when
+    // causal, its first key is at most r, so it never reads this tile's
+    // partials).
+    if (SPLIT && n_tiles == 0) return;
     __builtin_amdgcn_s_waitcnt(kWaitVm0);      // this wave's share of K_0 (and its Q rows)
     __syncthreads();
 
@@ -809,19 +802,35 @@ hipError_t launch(const FwdArgs& a, int n_splits, float* op, float* lp, hipStrea
 // (row, 4 consecutive d); kMergeRows rows per 256-thread block.
 constexpr int kMergeThreads = 256;
 
+// Number of key ranges that hold a key row r sees: the ranges with keys
+// (kq + 1 tiles for s < kr, kq after), and, when causal, only those whose
+// first key is at most r.  Range s starts at tile s (kq + 1) for s <= kr
+// and at s kq + kr after, so with t = r / bc those are the s with start <= t.
+// These are exactly the ranges whose partials the split kernel wrote for
+// the row; the merge reads no other.
+__device__ __forceinline__ int ranges_seen(int r, int n_splits, int kq, int kr, int bc, bool causal) {
+    const int with_keys = kq > 0 ? n_splits : kr;
+    if (!causal) return with_keys;
+    const int t = r / bc;
+    const int a = kr * (kq + 1);              // first tile of range kr
+    const int c = t < a ? t / (kq + 1) + 1 : (kq > 0 ? (t - kr) / kq + 1 : kr);
+    return min(c, with_keys);
+}
+
 template <int D>
 __global__ __launch_bounds__(kMergeThreads) void merge_splits_kernel(
     const float* __restrict__ OP, const float* __restrict__ LP, __bf16* __restrict__ O,
-    float* __restrict__ LSE, int n_splits, long long rows) {
+    float* __restrict__ LSE, int n_splits, long long rows, int N, int kq, int kr, int causal) {
     constexpr int TPR = D / 4;                        // threads per row
     const long long row = (long long)blockIdx.x * (kMergeThreads / TPR) + threadIdx.x / TPR;
     if (row >= rows) return;
     const int c4 = threadIdx.x % TPR;
+    const int ns = ranges_seen((int)(row % N), n_splits, kq, kr, Tile<D>::BC, causal != 0);
     float mx = -__builtin_inff();
-    for (int sp = 0; sp < n_splits; ++sp) mx = fmaxf(mx, LP[sp * rows + row]);
+    for (int sp = 0; sp < ns; ++sp) mx = fmaxf(mx, LP[sp * rows + row]);
     float wsum = 0.f;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int sp = 0; sp < n_splits; ++sp) {
+    for (int sp = 0; sp < ns; ++sp) {
         const float l = LP[sp * rows + row];
         const float w = l == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f((l - mx) * 1.4426950408889634f);
         const float4 x = *(const float4*)(OP + (sp * rows + row) * D + 4 * c4);
@@ -846,9 +855,12 @@ hipError_t launch_merge(const FwdArgs& a, int n_splits, const float* op, const f
                         hipStream_t stream) {
     long long rows = (long long)a.B * a.Hq * a.N;
     const long long per_block = kMergeThreads / (D / 4);
+    const int n_kt = (a.N + Tile<D>::BC - 1) / Tile<D>::BC;
+    int kq = n_kt / n_splits, kr = n_kt % n_splits;
+    int N = a.N, causal = a.causal;
     __bf16* o = (__bf16*)a.o;
     float* lse = a.lse;
-    void* args[] = {(void*)&op, (void*)&lp, &o, &lse, &n_splits, &rows};
+    void* args[] = {(void*)&op, (void*)&lp, &o, &lse, &n_splits, &rows, &N, &kq, &kr, &causal};
     return hipLaunchKernel((const void*)merge_splits_kernel<D>, dim3((unsigned)((rows + per_block - 1) / per_block)),
                            dim3(kMergeThreads), args, 0, stream);
 }
