@@ -124,12 +124,13 @@ CLOCK_LIB = os.path.join(ROOT, "io_aware_tiled_04_amd", "libfa_clock.so")
 class ClockProbe:
     """The shader clock under load: a one-wave probe kernel (libfa_clock.so)
     on a second stream, at the default priority, spins for a fixed window of
-    the GPU's constant-rate real-time counter while the timed launches run
-    and counts the shader-clock cycles that pass.  clock = cycles / window,
-    with the window timed by HIP events on the probe's stream.  The window
-    is made shorter than the timed region so that the probe sees only the
-    attention kernel's load.  ``mhz`` is None when the probe library is
-    missing or the window could not be timed."""
+    the GPU's constant-rate real-time counter while launches of the
+    attention kernel run, and counts the shader-clock cycles that pass.
+    clock = cycles / window, with the window timed by HIP events on the
+    probe's stream.  The caller keeps launching for longer than the window,
+    so that the probe sees only the attention kernel's load.  ``mhz`` is
+    None when the probe library is missing or the window could not be
+    timed."""
 
     def __init__(self, window_ms: float):
         import ctypes
@@ -170,7 +171,7 @@ class ClockProbe:
             self.realtime_mhz = rticks / (ms * 1e3)
 
 
-def summarize(d: str, skip: int = 0) -> None:
+def summarize(d: str, skip: int = 0, count: int = 0) -> None:
     """Per-kernel figures from a rocprofv3 output directory (its rocpd SQLite
     database): average dispatch duration from a kernel trace (leaving out
     each kernel's first ``skip`` dispatches, the warm-up), and per-dispatch
@@ -182,13 +183,16 @@ def summarize(d: str, skip: int = 0) -> None:
         con = sqlite3.connect(path)
         views = {r[0] for r in con.execute("select name from sqlite_master")}
         print(f"# {os.path.relpath(path, d)}" + (f" (first {skip} dispatches of each kernel left out)"
-                                                  if skip else ""))
+                                                  if skip else "")
+              + (f" (at most {count} dispatches of each kernel after those)" if count else ""))
         if "kernels" in views:
             per = {}
             for name, dur in con.execute("select name, duration from kernels order by start"):
                 per.setdefault(name, []).append(dur)
             for name, durs in sorted(per.items(), key=lambda kv: -sum(kv[1])):
                 kept = durs[skip:] if len(durs) > skip else durs
+                if count:
+                    kept = kept[:count]
                 print(f"trace | {name[:80]} | calls={len(kept)} avg_us={sum(kept) / len(kept) / 1e3:.2f} "
                       f"min_us={min(kept) / 1e3:.2f} max_us={max(kept) / 1e3:.2f}")
         if "counters_collection" in views:
@@ -222,6 +226,8 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--summarize", default=None)
+    ap.add_argument("--count", type=int, default=0,
+                    help="with --summarize: keep at most this many dispatches of each kernel after --skip")
     ap.add_argument("--skip", type=int, default=0,
                     help="with --summarize: leave out each kernel's first SKIP dispatches (the warm-up)")
     ap.add_argument("--splitkv", type=int, default=0,
@@ -234,7 +240,7 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.summarize:
-        summarize(args.summarize, args.skip)
+        summarize(args.summarize, args.skip, args.count)
         return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this forward pass shards over (batch, head) "
@@ -276,23 +282,15 @@ def main() -> int:
         if rc != fa.FA_OK:
             raise fa.FaError(rc)
 
-    w0 = torch.cuda.Event(enable_timing=True)
-    w1 = torch.cuda.Event(enable_timing=True)
-    w0.record(stream)
     for _ in range(args.warmup):
         launch()
-    w1.record(stream)
     torch.cuda.synchronize()
-    warm_ms = w0.elapsed_time(w1) / max(1, args.warmup)
-    # probe window: about 70% of the expected timed region, 0.5 .. 40 ms
-    clock = ClockProbe(min(40.0, max(0.5, 0.7 * warm_ms * args.steps)))
 
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     region0 = torch.cuda.Event(enable_timing=True)
     region1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    clock.start()
     wall0 = time.perf_counter()
     region0.record(stream)
     for i in range(args.steps):
@@ -302,10 +300,20 @@ def main() -> int:
     region1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    clock.finish()
     total_ms = region0.elapsed_time(region1)
     launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     avg_launch_ms = sum(launch_ms) / len(launch_ms)
+
+    # The shader clock under this load, probed after the timed region over
+    # extra untimed launches: the probe's wave holds a compute unit while it
+    # runs, which would slow the timed launches (a grid of whole rounds of
+    # workgroups, such as c3's 4 per CU, loses a fifth of a round).
+    clock = ClockProbe(10.0)
+    n_probe = int(12.0 / max(1e-3, launch_ms[-1])) + 2
+    clock.start()
+    for _ in range(n_probe):
+        launch()
+    clock.finish()
 
     if args.calibrate_copy:
         _calibrate_copy(dev)
@@ -366,7 +374,8 @@ def main() -> int:
                      "last5_tflops": round(flops / (last_us * 1e-6) / 1e12, 2),
                      "sclk_mhz": round(clk, 1) if clk else None,
                      "sclk_source": "s_memtime cycles of a one-wave probe on a second stream over "
-                                    f"{clock.window_ms:.1f} ms of the timed launches" if clk else None,
+                                    f"{clock.window_ms:.1f} ms of {n_probe} untimed launches right after the "
+                                    "timed ones" if clk else None,
                      "peak_at_sclk": round(clock_peak, 1) if clock_peak else None,
                      "frac_at_sclk": round(achieved / clock_peak, 4) if clock_peak else None},
         "parity": {"rows": len(rows), "max_abs_o": float(err.max()),
