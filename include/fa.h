@@ -64,7 +64,8 @@ enum fa_status {
     FA_ERR_ARG = -5,       /* scale is not finite, num_splits or p_drop is out of range */
     FA_ERR_HIP = -6,       /* the HIP runtime rejected the launch */
     FA_ERR_WORKSPACE = -7, /* a workspace argument is null, misaligned or too small */
-    FA_ERR_SCRATCH = -8    /* the problem needs more than the fixed scratch of fa_fwd_splitkv_noalloc */
+    FA_ERR_SCRATCH = -8,   /* the problem needs more than the fixed scratch of fa_fwd_splitkv_noalloc */
+    FA_ERR_ALIGN = -9      /* a tensor pointer is misaligned: 16 bytes for q, k, v, o, dout, dq, dk, dv; 4 for lse */
 };
 
 /* Bytes of the fixed device scratch array of fa_fwd_splitkv_noalloc (64 MiB). */
@@ -78,6 +79,9 @@ enum fa_status {
  *   even from its fp32 value.
  * lse [B,Hq,N]: float32 device pointer, written with the natural-log
  *   logsumexp of the scaled, masked scores of each query row.
+ * q, k, v and o must be 16-byte aligned (the kernels move whole 16-byte
+ * pieces of rows) and lse 4-byte aligned, or the call returns FA_ERR_ALIGN;
+ * the same holds for every entry point below (fp32 tensors included).
  * d in {64, 128}; N >= 1 (any length; partial tiles are masked).
  * Products Q K^T and P V run on bf16 matrix cores with fp32 accumulation; the
  * softmax state (row max, row sums, output accumulator) is fp32.  The

@@ -25,6 +25,9 @@ int validate(const void* q, const void* k, const void* v, const void* o, const v
     if (Hq % Hkv != 0) return FA_ERR_HEADS;
     if (d != 64 && d != 128) return FA_ERR_HEADDIM;
     if (!std::isfinite(scale)) return FA_ERR_ARG;
+    // the kernels move whole 16-byte pieces of rows
+    if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15) return FA_ERR_ALIGN;
+    if ((uintptr_t)lse & 3) return FA_ERR_ALIGN;
     return FA_OK;
 }
 
@@ -190,6 +193,7 @@ int check_bwd(const void* q, const void* k, const void* v, const void* o, const 
     if (!dout || !dq || !dk || !dv) return FA_ERR_NULL;
     const int rc = validate(q, k, v, o, lse, B, Hq, Hkv, N, d, scale);
     if (rc != FA_OK) return rc;
+    if (((uintptr_t)dout | (uintptr_t)dq | (uintptr_t)dk | (uintptr_t)dv) & 15) return FA_ERR_ALIGN;
     const long long bh = (long long)B * Hq;
     const long long rtiles = ((long long)N + fa::kBwdBlockRows - 1) / fa::kBwdBlockRows;
     if (bh * rtiles > INT_MAX) return FA_ERR_SHAPE;
@@ -263,6 +267,7 @@ extern "C" const char* fa_status_string(int status) {
         case FA_ERR_ARG: return "invalid scalar argument (scale must be finite, num_splits in 1..256, p_drop in [0, 1))";
         case FA_ERR_WORKSPACE: return "workspace is null, not 16-byte aligned or smaller than the size the entry point needs";
         case FA_ERR_SCRATCH: return "problem needs more than the 64 MiB fixed scratch of fa_fwd_splitkv_noalloc (use fewer splits or a workspace)";
+        case FA_ERR_ALIGN: return "a tensor pointer is misaligned (16 bytes for q, k, v, o, dout, dq, dk, dv; 4 bytes for lse)";
         case FA_ERR_HIP: return "HIP launch failed";
         default: return "unknown status";
     }

@@ -28,6 +28,7 @@ FA_ERR_ARG = -5
 FA_ERR_HIP = -6
 FA_ERR_WORKSPACE = -7
 FA_ERR_SCRATCH = -8
+FA_ERR_ALIGN = -9
 
 # Bytes of the fixed device scratch array of fa_fwd_splitkv_noalloc.
 FA_NOALLOC_SCRATCH_BYTES = 64 << 20

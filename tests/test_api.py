@@ -67,6 +67,12 @@ P = 0x1000
     ((P, P, P, P, P, 1, 1, 1, 128, 64, 1, math.nan), "FA_ERR_ARG"),
     ((P, P, P, P, P, 1, 1, 1, 128, 64, 1, math.inf), "FA_ERR_ARG"),
     ((P, P, P, P, P, 1, 1, 1, 128, 64, 1, -math.inf), "FA_ERR_ARG"),
+    # tensors are moved in whole 16-byte pieces; lse as 4-byte words
+    ((P + 8, P, P, P, P, 1, 1, 1, 128, 64, 1, 0.125), "FA_ERR_ALIGN"),
+    ((P, P + 2, P, P, P, 1, 1, 1, 128, 64, 1, 0.125), "FA_ERR_ALIGN"),
+    ((P, P, P + 4, P, P, 1, 1, 1, 128, 64, 1, 0.125), "FA_ERR_ALIGN"),
+    ((P, P, P, P + 1, P, 1, 1, 1, 128, 64, 1, 0.125), "FA_ERR_ALIGN"),
+    ((P, P, P, P, P + 2, 1, 1, 1, 128, 64, 1, 0.125), "FA_ERR_ALIGN"),
 ])
 def test_invalid_arguments_are_rejected(fn, args, expect):
     from io_aware_tiled_04_amd import fa
@@ -85,6 +91,7 @@ def test_splitkv_rejects_the_common_invalid_arguments():
         ((P, P, P, P, P, 1, 6, 4, 128, 64, 1, 0.125), "FA_ERR_HEADS"),
         ((P, P, P, P, P, 1, 1, 1, 128, 80, 1, 0.125), "FA_ERR_HEADDIM"),
         ((P, P, P, P, P, 1, 1, 1, 128, 64, 1, math.nan), "FA_ERR_ARG"),
+        ((P, P, P, P + 8, P, 1, 1, 1, 128, 64, 1, 0.125), "FA_ERR_ALIGN"),
     ]
     for args, expect in cases:
         rc = fa.fa_fwd_splitkv(*args, 2, P, W, 0)
@@ -176,6 +183,10 @@ def test_kvouter_validation_and_workspace_size():
     ((P,) * 9, (1, 2, 1, 128, 64, 1, math.inf), (P, 1 << 20), "FA_ERR_ARG"),
     ((P,) * 9, (1, 2, 1, 128, 64, 1, 0.125), (0, 1 << 20), "FA_ERR_WORKSPACE"),
     ((P,) * 9, (1, 2, 1, 128, 64, 1, 0.125), (P, 2 * 128 * 4 - 1), "FA_ERR_WORKSPACE"),
+    ((P, P, P, P, P, P + 8, P, P, P), (1, 2, 1, 128, 64, 1, 0.125), (P, 1 << 20), "FA_ERR_ALIGN"),
+    ((P, P, P, P, P, P, P + 2, P, P), (1, 2, 1, 128, 64, 1, 0.125), (P, 1 << 20), "FA_ERR_ALIGN"),
+    ((P, P, P, P, P, P, P, P, P + 4), (1, 2, 1, 128, 64, 1, 0.125), (P, 1 << 20), "FA_ERR_ALIGN"),
+    ((P, P, P, P, P + 1, P, P, P, P), (1, 2, 1, 128, 64, 1, 0.125), (P, 1 << 20), "FA_ERR_ALIGN"),
 ])
 def test_backward_rejects_invalid_arguments(ptrs, sizes, ws, expect):
     from io_aware_tiled_04_amd import fa

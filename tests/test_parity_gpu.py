@@ -403,3 +403,21 @@ def test_concurrent_streams_and_host_threads():
     for i in range(len(ws)):
         for o, lse in outs[i]:
             assert torch.equal(o, alone[i][0]) and torch.equal(lse, alone[i][1]), ws[i].name
+
+
+def test_misaligned_tensors_are_rejected_before_any_launch():
+    """Views that start 2 bytes into their storage (contiguous, bf16) are
+    refused with FA_ERR_ALIGN, and the output is left untouched."""
+    w = Workload("align", 1, 2, 2, 128, 64, False, "bf16", 93)
+    q, k, v = (t.to("cuda") for t in make_inputs(w))
+    fa = _fa()
+    shifted = torch.empty(q.numel() + 1, dtype=torch.bfloat16, device="cuda")[1:].view(q.shape)
+    shifted.copy_(q)
+    out = torch.full_like(q, 7.0)
+    lse = torch.full((1, 2, 128), 7.0, dtype=torch.float32, device="cuda")
+    _say("misaligned q rejected")
+    with pytest.raises(fa.FaError) as e:
+        fa.fwd(shifted, k, v, scale=w.scale, out=out, lse_out=lse)
+    assert e.value.status == fa.FA_ERR_ALIGN
+    torch.cuda.synchronize()
+    assert torch.all(out == 7.0) and torch.all(lse == 7.0)
