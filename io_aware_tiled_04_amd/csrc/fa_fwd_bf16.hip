@@ -479,7 +479,8 @@ __device__ __forceinline__ void softmax_tile(f32x16 (&s)[Tile<D>::KB], bf16x8 (&
 // element when scale < 0 (exact), so that the kernel only sees c_log2 > 0.
 //
 // SPLIT: the launch covers n_splits disjoint ranges of the T key tiles:
-// with kq = T / n_splits and kr = T % n_splits, split s = blockIdx.y takes
+// with kq = T / n_splits and kr = T % n_splits, split s = n_splits - 1 -
+// blockIdx.y (the last range first, see the work decomposition) takes
 // the tiles [s*kq + min(s, kr), (s+1)*kq + min(s+1, kr)) (kr ranges of kq+1
 // tiles, then ranges of kq).  Without SPLIT, kq = T and kr = 0.  Each workgroup then writes the fp32 partial result
 // of its range instead of O and LSE: the output normalised by its own row
@@ -521,8 +522,13 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     // causal) tiles first: four heads keep the K/V being read within the
     // XCD's L2 (half the L2 misses of rounds over all its heads, at the same
     // speed), and the short tiles of each group fill in behind the long ones.
+    // Split ranges go out last range first: when causal, a late range holds
+    // keys only for the late (long) query tiles, so the long pieces of work
+    // start first and the short ones (early ranges of early tiles, and the
+    // ranges a tile does not see at all, which return at once) fill in
+    // behind them.  All workgroups in flight still read one key range.
     int bh, qt;
-    const int split = SPLIT ? (int)blockIdx.y : 0;
+    const int split = SPLIT ? (int)(gridDim.y - 1 - blockIdx.y) : 0;
     {
         const int w = blockIdx.x;
         if ((bh_total & 31) == 0) {
