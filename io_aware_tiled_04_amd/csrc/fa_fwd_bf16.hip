@@ -526,7 +526,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     // keys only for the late (long) query tiles, so the long pieces of work
     // start first and the short ones (early ranges of early tiles, and the
     // ranges a tile does not see at all, which return at once) fill in
-    // behind them.  All workgroups in flight still read one key range.
+    // behind them.  Consecutive workgroups read one key range.
     int bh, qt;
     const int split = SPLIT ? (int)(gridDim.y - 1 - blockIdx.y) : 0;
     {
@@ -541,8 +541,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
             bh = (w & 7) * (bh_total >> 3) + slot % (bh_total >> 3);
             qt = slot / (bh_total >> 3);
         } else {
-            bh = w / n_qtiles;
-            qt = w % n_qtiles;
+            // (few heads) tile-major over all heads, so that when causal the
+            // long tiles of every head go out before the short ones of any
+            bh = w % bh_total;
+            qt = w / bh_total;
         }
         if (CAUSAL) qt = n_qtiles - 1 - qt;
     }
