@@ -247,8 +247,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
             bh = (w & 7) * (bh_total >> 3) + slot % (bh_total >> 3);
             rt = slot / (bh_total >> 3);
         } else {
-            bh = w / n_rtiles;
-            rt = w % n_rtiles;
+            // (few heads) tile-major over all heads: the long causal tiles
+            // of every head go out before the short ones of any
+            bh = w % bh_total;
+            rt = w / bh_total;
         }
         if (CAUSAL) rt = n_rtiles - 1 - rt;
     }
@@ -474,8 +476,10 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(
             bh = (w & 7) * (bh_total >> 3) + slot % (bh_total >> 3);
             rt = slot / (bh_total >> 3);
         } else {
-            bh = w / n_rtiles;
-            rt = w % n_rtiles;
+            // (few heads) tile-major over all heads, the long key blocks
+            // (first when causal) of every head before the short ones of any
+            bh = w % bh_total;
+            rt = w / bh_total;
         }
     }
     const int b = bh / Hkv;
