@@ -28,7 +28,7 @@
 // holds two of them.  S and dP are computed twice in all (once for dQ, once
 // for dK and dV): 7 products for the 5 of the definition.
 // Streamed tiles are 32 rows, double-buffered in LDS and loaded into
-// registers one tile ahead.
+// registers one step ahead; a dQ step takes one tile, a dK/dV step two.
 //
 // Dropout (DROP): the forward's output was O = (P (.) Z) V / (1 - p), so with
 // f = 1 / (1 - p),  dV = (P (.) Z)^T dO f,  dP = (dO V^T) (.) Z f, and
@@ -420,27 +420,32 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
 
 // dK and dV in one launch.  A workgroup of 8 waves holds 128 resident keys,
 // 32 per wave pair (wave w and w + 4), and streams the query tiles of the
-// GQA group once for both waves of every pair.  Per 32-row step:
+// GQA group once for both waves of every pair, kSub 32-row tiles per step.
+// Per step, for each of its tiles:
 //   first half:  wave w     S = Q K^T (8 MFMAs), P (exp), P out to LDS;
 //                wave w+4   dP = dO V^T (8 MFMAs), dP out to LDS;
 //   barrier;
 //   second half: wave w     dS = P (.) (dP - D), dK^T += Q^T dS (8 MFMAs);
-//                wave w+4   dV^T += dO^T P (8 MFMAs);  next tile to LDS;
+//                wave w+4   dV^T += dO^T P (8 MFMAs);  next step's tiles to LDS;
 //   barrier.
-// So each SIMD (one wave of each kind) has 16 MFMAs in each half, and S and
-// dP are computed once per pair (the separate DK and DV kernels computed S
-// twice and streamed Q and dO twice).  P goes over in bf16 (it is rounded so
-// for the products anyway, thinned by dropout); dP in fp32.
+// So each SIMD (one wave of each kind) has 16 kSub MFMAs in each half, and S
+// and dP are computed once per pair (the separate DK and DV kernels computed
+// S twice and streamed Q and dO twice).  P goes over in bf16 (it is rounded
+// so for the products anyway, thinned by dropout); dP in fp32.  Two tiles
+// per step halve the barriers, exchanges and pipeline fills per MFMA.
+constexpr int kSub = 2;
 template <int D>
 struct Lay2 {
     static constexpr int RBYTES = kTile * 2 * D;
-    static constexpr int A = 0;                           // Q rows
-    static constexpr int B = RBYTES;                      // dO rows
-    static constexpr int S = 2 * RBYTES;                  // LSE*log2e and D of the 32 rows
-    static constexpr int SET = S + 2 * kTile * 4;
-    static constexpr int PXP = 2 * SET;                   // P:  [4 pairs][2 chunks][64 lanes] x 16 B
-    static constexpr int PXD = PXP + 4 * 2 * 64 * 16;     // dP: [4 pairs][4 quads][64 lanes] x 16 B
-    static constexpr int BYTES = PXD + 4 * 4 * 64 * 16;
+    // one buffer set: for tile j of the step, Q rows at A(j), dO rows at
+    // B(j), LSE*log2e and D of its 32 rows at S(j)
+    static constexpr int A(int j) { return j * 2 * RBYTES; }
+    static constexpr int B(int j) { return j * 2 * RBYTES + RBYTES; }
+    static constexpr int S(int j) { return kSub * 2 * RBYTES + j * 2 * kTile * 4; }
+    static constexpr int SET = kSub * (2 * RBYTES + 2 * kTile * 4);
+    static constexpr int PXP = 2 * SET;                          // P:  [4 pairs][kSub][2 chunks][64 lanes] x 16 B
+    static constexpr int PXD = PXP + 4 * kSub * 2 * 64 * 16;     // dP: [4 pairs][kSub][4 quads][64 lanes] x 16 B
+    static constexpr int BYTES = PXD + 4 * kSub * 4 * 64 * 16;
 };
 constexpr int kDkvThreads = 512;
 
@@ -453,6 +458,7 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(
     using L = Lay2<D>;
     constexpr int KS = D / 16;
     constexpr int DB = D / 32;
+    static_assert(L::BYTES <= 160 * 1024, "fits the LDS of one compute unit");
 
     __shared__ __attribute__((aligned(16))) char smem_raw[L::BYTES];
     LDS char* smem = (LDS char*)smem_raw;
@@ -505,34 +511,44 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(
 #pragma unroll
     for (int db = 0; db < DB; ++db) acc[db] = (f32x16){};
 
+    // Streamed 32-row tiles t_begin .. t_end-1 of each query head of the
+    // group, kSub per step (the last step of a head may hold fewer: its
+    // missing tiles lie past t_end and are skipped).
     const int t_begin = CAUSAL ? r0 / kTile : 0;
     const int t_end = (N + kTile - 1) / kTile;
-    const int per_head = max(0, t_end - t_begin);
+    const int per_head = max(0, (t_end - t_begin + kSub - 1) / kSub);
     const int n_steps = group * per_head;
     auto q_head = [&](int hs) -> size_t { return ((size_t)b * Hq + hr * group + hs) * N; };
+    // first tile of step st (in tiles), and its query head
+    auto step_tile = [&](int st) { return t_begin + kSub * (st % per_head); };
 
     // Copies: threads 0-255 stage Q rows, 256-511 dO rows (item it = tid & 255),
-    // threads 0-31 also the row statistics.
+    // threads 0-63 also the row statistics (tile tid / 32 of the step).
     const int ct = tid & 255;
     const bool copy_do = tid >= 256;
-    u32x4 x0, x1;
+    u32x4 x0[kSub], x1[kSub];
     float s0 = 0.f, s1 = 0.f;
     int srow = 0;
     auto load_step = [&](int step) __attribute__((always_inline)) {
         const int st = min(step, n_steps - 1);
         const int hs = st / per_head;
-        const int row0 = (t_begin + st % per_head) * kTile;
-        stage_rows<D>((copy_do ? dO : Q) + q_head(hs) * D, row0, N, ct, x0, x1);
-        if (tid < kTile) stage_stats(LSE + q_head(hs), Dd + q_head(hs), row0, N, tid, s0, s1, srow);
+        const int tile0 = step_tile(st);
+#pragma unroll
+        for (int j = 0; j < kSub; ++j)
+            stage_rows<D>((copy_do ? dO : Q) + q_head(hs) * D, (tile0 + j) * kTile, N, ct, x0[j], x1[j]);
+        if (tid < kSub * kTile)
+            stage_stats(LSE + q_head(hs), Dd + q_head(hs), (tile0 + tid / kTile) * kTile, N, tid, s0, s1, srow);
     };
     auto store_step = [&](int set) __attribute__((always_inline)) {
         LDS char* base = smem + set * L::SET;
-        put_rows<D>(base + (copy_do ? L::B : L::A), ct, x0, x1);
-        if (tid < kTile) {
+#pragma unroll
+        for (int j = 0; j < kSub; ++j) put_rows<D>(base + (copy_do ? L::B(j) : L::A(j)), ct, x0[j], x1[j]);
+        if (tid < kSub * kTile) {
             float lse2, dv;
             finish_stats(s0, s1, srow, N, lse2, dv);
-            ((LDS float*)(base + L::S))[tid] = lse2;
-            ((LDS float*)(base + L::S))[kTile + tid] = dv;
+            LDS float* st = (LDS float*)(base + L::S(tid / kTile));
+            st[tid % kTile] = lse2;
+            st[kTile + tid % kTile] = dv;
         }
     };
 
@@ -543,28 +559,37 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(
     }
     __syncthreads();
 
-    LDS bf16x8* pxp = (LDS bf16x8*)(smem + L::PXP) + wb * 128;   // [cc][lane]
-    const int mine = dk_role ? L::A : L::B;                      // the streamed tile this wave reads
     const int rowop = rowop_off<D>(lane);
     const int trop0 = trop_off<D>(lane, 0), trop1 = trop_off<D>(lane, 1);
-    LDS f32x4* pxd = (LDS f32x4*)(smem + L::PXD) + wb * 256;     // [quad][lane]
 
 #pragma unroll 1
     for (int step = 0; step < n_steps; ++step) {
         const int set = step & 1;
         const LDS char* base = smem + set * L::SET;
-        const int row0 = (t_begin + step % per_head) * kTile;
-        bool active = wr0 < N;
-        bool masked = row0 + kTile > N || wr0 + 32 > N;
-        if (CAUSAL) {
-            active = active && row0 + kTile - 1 >= wr0;
-            masked = masked || row0 < wr0 + 31;
+        const int tile0 = step_tile(step);
+        const int hs = step / per_head;
+        bool active[kSub], masked[kSub];
+#pragma unroll
+        for (int j = 0; j < kSub; ++j) {
+            const int row0 = (tile0 + j) * kTile;
+            active[j] = tile0 + j < t_end && wr0 < N;
+            masked[j] = row0 + kTile > N || wr0 + 32 > N;
+            if (CAUSAL) {
+                active[j] = active[j] && row0 + kTile - 1 >= wr0;
+                masked[j] = masked[j] || row0 < wr0 + 31;
+            }
         }
         // register i of a 32x32 accumulator: streamed row (i/4)*8 + 4h + i%4 of the
         // tile (a query), resident key my_row (the lane)
-        float p[16];
-        uint32_t zword = 0;
-        if (active) {
+        float p[kSub][16];
+        uint32_t zword[kSub] = {};
+#pragma unroll
+        for (int j = 0; j < kSub; ++j) {
+            if (!active[j]) continue;
+            const int row0 = (tile0 + j) * kTile;
+            LDS bf16x8* pxp = (LDS bf16x8*)(smem + L::PXP) + (wb * kSub + j) * 128;   // [cc][lane]
+            LDS f32x4* pxd = (LDS f32x4*)(smem + L::PXD) + (wb * kSub + j) * 256;     // [quad][lane]
+            const int mine = dk_role ? L::A(j) : L::B(j);                            // the streamed tile this wave reads
             bf16x8 fa[KS];
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) fa[ks] = *(const LDS bf16x8*)(base + mine + (rowop ^ (32 * ks)));
@@ -584,8 +609,8 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(
                     // all taken
                     uint32_t k0 = dr.k0, k1 = dr.k1, m0 = kPhiloxM0, m1 = kPhiloxM1;
                     asm volatile("" : "+v"(k0), "+v"(k1), "+v"(m0), "+v"(m1));
-                    const uint32_t bhq = (uint32_t)(b * Hq + hr * group + step / per_head);
-                    uint32_t mine = 0;
+                    const uint32_t bhq = (uint32_t)(b * Hq + hr * group + hs);
+                    uint32_t mine_bits = 0;
                     uint32_t ctr0 = (uint32_t)(2 * (wr0 >> 4) + h);
                     asm volatile("" : "+v"(ctr0));
 #pragma unroll
@@ -594,20 +619,21 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(
                             philox4x32_10(ctr0 + 2 * al, (uint32_t)(row0 + l32), bhq, dr.offset, k0, k1, m0, m1);
 #pragma unroll
                         for (int k = 0; k < 8; ++k)
-                            mine |= (uint32_t)keep_half(r.w[k >> 1], k & 1, t) << (8 * al + k);
+                            mine_bits |= (uint32_t)keep_half(r.w[k >> 1], k & 1, t) << (8 * al + k);
                     }
                     const int pos = ((l32 >> 4) << 3) | (((l32 >> 3) & 1) << 2) | (l32 & 3);
                     uint32_t sel = 1u << pos;
                     uint32_t sh = ((l32 >> 2) & 1) * 32u;
                     asm volatile("" : "+v"(sel), "+v"(sh));
+                    uint32_t zw = 0;
 #pragma unroll
                     for (int bit = 0; bit < 16; ++bit) {
-                        const uint64_t bal = __builtin_amdgcn_ballot_w64((mine >> bit) & 1u);
-                        zword |= (uint32_t)(bal >> sh) & (0u - ((sel >> bit) & 1u));
+                        const uint64_t bal = __builtin_amdgcn_ballot_w64((mine_bits >> bit) & 1u);
+                        zw |= (uint32_t)(bal >> sh) & (0u - ((sel >> bit) & 1u));
                     }
-                    zword >>= 4 * h;
+                    zword[j] = zw >> (4 * h);
                 }
-                const LDS float* st = (const LDS float*)(base + L::S);
+                const LDS float* st = (const LDS float*)(base + L::S(j));
                 float arg[16];
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
@@ -617,7 +643,7 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(
                 }
                 // Dead scores get exp2(-inf) = 0: selects under one uniform
                 // branch, not a branch around each exponential.
-                if (masked) {
+                if (masked[j]) {
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {
                         const int qry = row0 + 8 * (i >> 2) + 4 * h + (i & 3);
@@ -628,17 +654,22 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(
                 bf16x8 pw[2];
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    p[i] = __builtin_amdgcn_exp2f(arg[i]);
+                    p[j][i] = __builtin_amdgcn_exp2f(arg[i]);
                     // keep bit as a 0/1 multiplier (no condition registers held)
-                    const float keepf = DROP ? (float)((zword >> (8 * (i >> 2) + (i & 3))) & 1u) : 1.f;
-                    pw[i >> 3][i & 7] = (__bf16)(p[i] * keepf);
+                    const float keepf = DROP ? (float)((zword[j] >> (8 * (i >> 2) + (i & 3))) & 1u) : 1.f;
+                    pw[i >> 3][i & 7] = (__bf16)(p[j][i] * keepf);
                 }
                 pxp[lane] = pw[0];
                 pxp[64 + lane] = pw[1];
             }
         }
         __syncthreads();
-        if (active) {
+#pragma unroll
+        for (int j = 0; j < kSub; ++j) {
+            if (!active[j]) continue;
+            const LDS bf16x8* pxp = (const LDS bf16x8*)(smem + L::PXP) + (wb * kSub + j) * 128;
+            const LDS f32x4* pxd = (const LDS f32x4*)(smem + L::PXD) + (wb * kSub + j) * 256;
+            const int mine = dk_role ? L::A(j) : L::B(j);
             // operands of dK^T += (Q^T) dS  or  dV^T += (dO^T) P, read first so
             // that they arrive during the dS arithmetic
             bf16x8 ft[2 * DB];
@@ -646,7 +677,7 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(
             for (int i = 0; i < 2 * DB; ++i) ft[i] = tr_operand<D>(base + mine, trop0, trop1, i >> 1, i & 1);
             bf16x8 w[2];
             if (dk_role) {             // dS from the partner's dP
-                const LDS float* st = (const LDS float*)(base + L::S);
+                const LDS float* st = (const LDS float*)(base + L::S(j));
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
                     const f32x4 dp = pxd[g * 64 + lane];
@@ -656,10 +687,10 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(
                         const int i = 4 * g + e;
                         float val;
                         if constexpr (DROP) {
-                            const float keepf = (float)((zword >> (8 * g + e)) & 1u) * dr.factor;
-                            val = p[i] * fmaf(dp[e], keepf, -d4[e]);
+                            const float keepf = (float)((zword[j] >> (8 * g + e)) & 1u) * dr.factor;
+                            val = p[j][i] * fmaf(dp[e], keepf, -d4[e]);
                         } else {
-                            val = p[i] * (dp[e] - d4[e]);
+                            val = p[j][i] * (dp[e] - d4[e]);
                         }
                         w[i >> 3][i & 7] = (__bf16)val;
                     }
