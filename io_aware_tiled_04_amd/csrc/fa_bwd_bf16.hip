@@ -15,11 +15,13 @@
 // forward; D is the diag(dO O^T) term of the blog's standard backward).
 //
 // Kernels.
-//   D:   rowdot kernel, D_i = sum_d dO_id O_id.
 //   dQ:  resident query rows, streamed key tiles: S^T = K Q^T and
 //        dP^T = V dO^T put one query per lane (LSE and D per lane), and
 //        dQ^T += K^T dS^T takes K^T from LDS in the key order of dS^T's
-//        registers (the forward's V^T trick).  4 waves of 32 rows.
+//        registers (the forward's V^T trick).  4 waves of 32 rows.  It
+//        also forms D_i = sum_d dO_id O_id of its rows (it holds their dO)
+//        and leaves D in the workspace for the dK/dV kernel, which runs
+//        after it.
 //   dK, dV: one launch (bwd_dkv_kernel below): resident key rows, streamed
 //        query tiles, 8 waves in pairs: one wave of a pair forms S, P and
 //        then dS and dK, the other dP and then dV, exchanging P and dP
@@ -193,36 +195,16 @@ __device__ __forceinline__ void finish_stats(float s0, float s1, int srow, int n
     dv = in ? s1 : 0.f;
 }
 
-// D_i = sum_d dO_id O_id for every row: D / 8 threads per row, one 16-byte
-// chunk each, reduced across those threads.
-template <int D>
-__global__ __launch_bounds__(256) void bwd_rowdot_kernel(const __bf16* __restrict__ dO,
-                                                         const __bf16* __restrict__ O,
-                                                         float* __restrict__ Dout, long long rows) {
-    constexpr int TPR = D / 8;
-    const long long row = (long long)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
-    const int c = threadIdx.x % TPR;
-    float acc = 0.f;
-    if (row < rows) {
-        const bf16x8 a = *(const bf16x8*)(dO + row * D + 8 * c);
-        const bf16x8 b = *(const bf16x8*)(O + row * D + 8 * c);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc += (float)a[e] * (float)b[e];
-    }
-#pragma unroll
-    for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, TPR);
-    if (row < rows && c == 0) Dout[row] = acc;
-}
-
 // dQ: resident query rows of head hq, streamed key tiles of K/V head
-// hq / group.  c = scale * log2(e) (signed).  LSE and D are [B, Hq, N] float32.
+// hq / group.  c = scale * log2(e) (signed).  LSE and D are [B, Hq, N] float32;
+// the kernel writes D of its rows (from dO and the forward's output O).
 // DROP: the forward ran with dropout `dr` (see the file header).
 template <int D, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
-    const __bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dd,
-    __bf16* __restrict__ G, int Hq, int Hkv, int N, int n_rtiles, int bh_total, float c, float scale,
-    Dropout dr) {
+    const __bf16* __restrict__ dO, const __bf16* __restrict__ O, const float* __restrict__ LSE,
+    float* __restrict__ Dd, __bf16* __restrict__ G, int Hq, int Hkv, int N, int n_rtiles, int bh_total,
+    float c, float scale, Dropout dr) {
     using L = Lay<D>;
     constexpr int KS = D / 16;
     constexpr int DB = D / 32;
@@ -264,23 +246,22 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     // holds d = 16*ks + 8*h .. +7 of its row.
     const size_t rhead = ((size_t)b * Hq + hr) * N * D;
     bf16x8 rf1[KS], rf2[KS];
+    u32x4 orow[KS];                                      // the same d of the row of O
     {
         const int rr = min(my_row, N - 1);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             u32x4 x = *(const u32x4*)(Q + rhead + (size_t)rr * D + 16 * ks + 8 * h);
             u32x4 y = *(const u32x4*)(dO + rhead + (size_t)rr * D + 16 * ks + 8 * h);
+            orow[ks] = *(const u32x4*)(O + rhead + (size_t)rr * D + 16 * ks + 8 * h);
             if (my_row >= N) x = y = (u32x4){0u, 0u, 0u, 0u};
             rf1[ks] = __builtin_bit_cast(bf16x8, x);
             rf2[ks] = __builtin_bit_cast(bf16x8, y);
         }
     }
-    float lse2_lane, d_lane;
-    {
-        const size_t srow = ((size_t)b * Hq + hr) * N + min(my_row, N - 1);
-        lse2_lane = LSE[srow] * kLog2e;
-        d_lane = Dd[srow];
-    }
+    const size_t srow = ((size_t)b * Hq + hr) * N + min(my_row, N - 1);
+    float lse2_lane = LSE[srow] * kLog2e;
+    float d_lane;
 
     f32x16 acc[DB];
 #pragma unroll
@@ -309,6 +290,21 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     // always visible.
     load_step(0);
     store_step(0);
+    // D of this lane's row: its 64 d (those of its dO fragments, zero past
+    // N), then the other half from lane l ^ 32.  The loads of O arrived with
+    // (before) the first tile's.
+    {
+        float part = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const bf16x8 ov = __builtin_bit_cast(bf16x8, orow[ks]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) part = fmaf((float)rf2[ks][e], (float)ov[e], part);
+        }
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false);
+        d_lane = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+        if (h == 0 && my_row < N) Dd[srow] = d_lane;
+    }
     // The row statistics arrived with (before) the first tile.  Redefining
     // them here tells the compiler so; otherwise it cannot prove it on every
     // path into the loop and waits for all loads in flight at their first
@@ -744,7 +740,7 @@ hipError_t launch_dkv(const BwdArgs& a, const float* dd, const Dropout& drop, hi
 }
 
 template <int D, bool CAUSAL, bool DROP>
-hipError_t launch_dq(const BwdArgs& a, const float* dd, const Dropout& drop, hipStream_t stream) {
+hipError_t launch_dq(const BwdArgs& a, float* dd, const Dropout& drop, hipStream_t stream) {
     int n_rtiles = (a.N + kRows - 1) / kRows;
     int bh_total = a.B * a.Hq;
     float c = a.scale * kLog2e;
@@ -757,25 +753,19 @@ hipError_t launch_dq(const BwdArgs& a, const float* dd, const Dropout& drop, hip
     const float* lse = a.lse;
     __bf16* g = (__bf16*)a.dq;
     Dropout dr = drop;
-    void* args[] = {(void*)&q, (void*)&k, (void*)&v, (void*)&dO, (void*)&lse, (void*)&dd, &g,
+    const __bf16* o = (const __bf16*)a.o;
+    void* args[] = {(void*)&q, (void*)&k, (void*)&v, (void*)&dO, (void*)&o, (void*)&lse, (void*)&dd, &g,
                     &Hq, &Hkv, &N, &n_rtiles, &bh_total, &c, &scale, &dr};
     return hipLaunchKernel((const void*)bwd_dq_kernel<D, CAUSAL, DROP>, dim3(bh_total * n_rtiles),
                            dim3(kThreads), args, 0, stream);
 }
 
+// dQ first: it writes D, which the dK/dV kernel reads.
 template <int D, bool CAUSAL, bool DROP>
 hipError_t launch_all(const BwdArgs& a, float* workspace, const Dropout& dr, hipStream_t stream) {
-    long long rows = (long long)a.B * a.Hq * a.N;
-    const __bf16* dO = (const __bf16*)a.dO;
-    const __bf16* o = (const __bf16*)a.o;
     float* dd = workspace;
-    void* args[] = {(void*)&dO, (void*)&o, &dd, &rows};
-    const long long per_block = 256 / (D / 8);
-    hipError_t e = hipLaunchKernel((const void*)bwd_rowdot_kernel<D>,
-                                   dim3((unsigned)((rows + per_block - 1) / per_block)), dim3(256), args,
-                                   0, stream);
+    hipError_t e = launch_dq<D, CAUSAL, DROP>(a, dd, dr, stream);
     if (e != hipSuccess) return e;
-    if ((e = launch_dq<D, CAUSAL, DROP>(a, dd, dr, stream)) != hipSuccess) return e;
     return launch_dkv<D, CAUSAL, DROP>(a, dd, dr, stream);
 }
 
