@@ -30,7 +30,8 @@
 // holds two of them.  S and dP are computed twice in all (once for dQ, once
 // for dK and dV): 7 products for the 5 of the definition.
 // Streamed tiles are 32 rows, double-buffered in LDS and loaded into
-// registers one step ahead; a dQ step takes one tile, a dK/dV step two.
+// registers one step ahead; a dQ step takes one tile, a dK/dV step
+// kSub<D> of them (two at d = 128, three at d = 64).
 //
 // Dropout (DROP): the forward's output was O = (P (.) Z) V / (1 - p), so with
 // f = 1 / (1 - p),  dV = (P (.) Z)^T dO f,  dP = (dO V^T) (.) Z f, and
@@ -416,7 +417,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
 
 // dK and dV in one launch.  A workgroup of 8 waves holds 128 resident keys,
 // 32 per wave pair (wave w and w + 4), and streams the query tiles of the
-// GQA group once for both waves of every pair, kSub 32-row tiles per step.
+// GQA group once for both waves of every pair, kSub<D> 32-row tiles per step.
 // Per step, for each of its tiles:
 //   first half:  wave w     S = Q K^T (8 MFMAs), P (exp), P out to LDS;
 //                wave w+4   dP = dO V^T (8 MFMAs), dP out to LDS;
@@ -424,12 +425,13 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
 //   second half: wave w     dS = P (.) (dP - D), dK^T += Q^T dS (8 MFMAs);
 //                wave w+4   dV^T += dO^T P (8 MFMAs);  next step's tiles to LDS;
 //   barrier.
-// So each SIMD (one wave of each kind) has 16 kSub MFMAs in each half, and S
+// So each SIMD (one wave of each kind) has 16 kSub<D> MFMAs in each half, and S
 // and dP are computed once per pair (the separate DK and DV kernels computed
 // S twice and streamed Q and dO twice).  P goes over in bf16 (it is rounded
-// so for the products anyway, thinned by dropout); dP in fp32.  Two tiles
-// per step halve the barriers, exchanges and pipeline fills per MFMA.
-constexpr int kSub = 2;
+// so for the products anyway, thinned by dropout); dP in fp32.  Several tiles
+// per step cut the barriers, exchanges and pipeline fills per MFMA.
+template <int D>
+constexpr int kSub = D == 64 ? 3 : 2;     // as many as the LDS and registers hold
 template <int D>
 struct Lay2 {
     static constexpr int RBYTES = kTile * 2 * D;
@@ -437,11 +439,11 @@ struct Lay2 {
     // B(j), LSE*log2e and D of its 32 rows at S(j)
     static constexpr int A(int j) { return j * 2 * RBYTES; }
     static constexpr int B(int j) { return j * 2 * RBYTES + RBYTES; }
-    static constexpr int S(int j) { return kSub * 2 * RBYTES + j * 2 * kTile * 4; }
-    static constexpr int SET = kSub * (2 * RBYTES + 2 * kTile * 4);
-    static constexpr int PXP = 2 * SET;                          // P:  [4 pairs][kSub][2 chunks][64 lanes] x 16 B
-    static constexpr int PXD = PXP + 4 * kSub * 2 * 64 * 16;     // dP: [4 pairs][kSub][4 quads][64 lanes] x 16 B
-    static constexpr int BYTES = PXD + 4 * kSub * 4 * 64 * 16;
+    static constexpr int S(int j) { return kSub<D> * 2 * RBYTES + j * 2 * kTile * 4; }
+    static constexpr int SET = kSub<D> * (2 * RBYTES + 2 * kTile * 4);
+    static constexpr int PXP = 2 * SET;                          // P:  [4 pairs][kSub<D>][2 chunks][64 lanes] x 16 B
+    static constexpr int PXD = PXP + 4 * kSub<D> * 2 * 64 * 16;     // dP: [4 pairs][kSub<D>][4 quads][64 lanes] x 16 B
+    static constexpr int BYTES = PXD + 4 * kSub<D> * 4 * 64 * 16;
 };
 constexpr int kDkvThreads = 512;
 
@@ -508,21 +510,21 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(
     for (int db = 0; db < DB; ++db) acc[db] = (f32x16){};
 
     // Streamed 32-row tiles t_begin .. t_end-1 of each query head of the
-    // group, kSub per step (the last step of a head may hold fewer: its
+    // group, kSub<D> per step (the last step of a head may hold fewer: its
     // missing tiles lie past t_end and are skipped).
     const int t_begin = CAUSAL ? r0 / kTile : 0;
     const int t_end = (N + kTile - 1) / kTile;
-    const int per_head = max(0, (t_end - t_begin + kSub - 1) / kSub);
+    const int per_head = max(0, (t_end - t_begin + kSub<D> - 1) / kSub<D>);
     const int n_steps = group * per_head;
     auto q_head = [&](int hs) -> size_t { return ((size_t)b * Hq + hr * group + hs) * N; };
     // first tile of step st (in tiles), and its query head
-    auto step_tile = [&](int st) { return t_begin + kSub * (st % per_head); };
+    auto step_tile = [&](int st) { return t_begin + kSub<D> * (st % per_head); };
 
     // Copies: threads 0-255 stage Q rows, 256-511 dO rows (item it = tid & 255),
     // threads 0-63 also the row statistics (tile tid / 32 of the step).
     const int ct = tid & 255;
     const bool copy_do = tid >= 256;
-    u32x4 x0[kSub], x1[kSub];
+    u32x4 x0[kSub<D>], x1[kSub<D>];
     float s0 = 0.f, s1 = 0.f;
     int srow = 0;
     auto load_step = [&](int step) __attribute__((always_inline)) {
@@ -530,16 +532,16 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(
         const int hs = st / per_head;
         const int tile0 = step_tile(st);
 #pragma unroll
-        for (int j = 0; j < kSub; ++j)
+        for (int j = 0; j < kSub<D>; ++j)
             stage_rows<D>((copy_do ? dO : Q) + q_head(hs) * D, (tile0 + j) * kTile, N, ct, x0[j], x1[j]);
-        if (tid < kSub * kTile)
+        if (tid < kSub<D> * kTile)
             stage_stats(LSE + q_head(hs), Dd + q_head(hs), (tile0 + tid / kTile) * kTile, N, tid, s0, s1, srow);
     };
     auto store_step = [&](int set) __attribute__((always_inline)) {
         LDS char* base = smem + set * L::SET;
 #pragma unroll
-        for (int j = 0; j < kSub; ++j) put_rows<D>(base + (copy_do ? L::B(j) : L::A(j)), ct, x0[j], x1[j]);
-        if (tid < kSub * kTile) {
+        for (int j = 0; j < kSub<D>; ++j) put_rows<D>(base + (copy_do ? L::B(j) : L::A(j)), ct, x0[j], x1[j]);
+        if (tid < kSub<D> * kTile) {
             float lse2, dv;
             finish_stats(s0, s1, srow, N, lse2, dv);
             LDS float* st = (LDS float*)(base + L::S(tid / kTile));
@@ -564,9 +566,9 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(
         const LDS char* base = smem + set * L::SET;
         const int tile0 = step_tile(step);
         const int hs = step / per_head;
-        bool active[kSub], masked[kSub];
+        bool active[kSub<D>], masked[kSub<D>];
 #pragma unroll
-        for (int j = 0; j < kSub; ++j) {
+        for (int j = 0; j < kSub<D>; ++j) {
             const int row0 = (tile0 + j) * kTile;
             active[j] = tile0 + j < t_end && wr0 < N;
             masked[j] = row0 + kTile > N || wr0 + 32 > N;
@@ -577,14 +579,14 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(
         }
         // register i of a 32x32 accumulator: streamed row (i/4)*8 + 4h + i%4 of the
         // tile (a query), resident key my_row (the lane)
-        float p[kSub][16];
-        uint32_t zword[kSub] = {};
+        float p[kSub<D>][16];
+        uint32_t zword[kSub<D>] = {};
 #pragma unroll
-        for (int j = 0; j < kSub; ++j) {
+        for (int j = 0; j < kSub<D>; ++j) {
             if (!active[j]) continue;
             const int row0 = (tile0 + j) * kTile;
-            LDS bf16x8* pxp = (LDS bf16x8*)(smem + L::PXP) + (wb * kSub + j) * 128;   // [cc][lane]
-            LDS f32x4* pxd = (LDS f32x4*)(smem + L::PXD) + (wb * kSub + j) * 256;     // [quad][lane]
+            LDS bf16x8* pxp = (LDS bf16x8*)(smem + L::PXP) + (wb * kSub<D> + j) * 128;   // [cc][lane]
+            LDS f32x4* pxd = (LDS f32x4*)(smem + L::PXD) + (wb * kSub<D> + j) * 256;     // [quad][lane]
             const int mine = dk_role ? L::A(j) : L::B(j);                            // the streamed tile this wave reads
             bf16x8 fa[KS];
 #pragma unroll
@@ -661,10 +663,10 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(
         }
         __syncthreads();
 #pragma unroll
-        for (int j = 0; j < kSub; ++j) {
+        for (int j = 0; j < kSub<D>; ++j) {
             if (!active[j]) continue;
-            const LDS bf16x8* pxp = (const LDS bf16x8*)(smem + L::PXP) + (wb * kSub + j) * 128;
-            const LDS f32x4* pxd = (const LDS f32x4*)(smem + L::PXD) + (wb * kSub + j) * 256;
+            const LDS bf16x8* pxp = (const LDS bf16x8*)(smem + L::PXP) + (wb * kSub<D> + j) * 128;
+            const LDS f32x4* pxd = (const LDS f32x4*)(smem + L::PXD) + (wb * kSub<D> + j) * 256;
             const int mine = dk_role ? L::A(j) : L::B(j);
             // operands of dK^T += (Q^T) dS  or  dV^T += (dO^T) P, read first so
             // that they arrive during the dS arithmetic
