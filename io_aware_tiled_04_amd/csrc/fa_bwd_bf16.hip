@@ -29,9 +29,10 @@
 // The accumulator of one 32-row block at d = 128 takes 64 VGPRs, so no wave
 // holds two of them.  S and dP are computed twice in all (once for dQ, once
 // for dK and dV): 7 products for the 5 of the definition.
-// Streamed tiles are 32 rows, double-buffered in LDS and loaded into
-// registers one step ahead; a dQ step takes one tile, a dK/dV step
-// kSub<D> of them (two at d = 128, three at d = 64).
+// Streamed tiles are 32 rows, double-buffered in LDS and copied straight
+// from global memory into LDS one step ahead (direct loads, no registers);
+// a dQ step takes one tile, a dK/dV step kSub<D> of them (two at d = 128,
+// three at d = 64).
 //
 // Dropout (DROP): the forward's output was O = (P (.) Z) V / (1 - p), so with
 // f = 1 / (1 - p),  dV = (P (.) Z)^T dO f,  dP = (dO V^T) (.) Z f, and
@@ -65,6 +66,9 @@ constexpr int kRows = 32 * kWaves;      // resident rows per workgroup
 static_assert(kRows == kBwdBlockRows, "grid and kernel disagree on the resident tile");
 constexpr int kTile = 32;               // streamed rows per step
 constexpr float kLog2e = 1.4426950408889634f;
+// s_waitcnt immediate that waits for all vector memory operations only
+// (vmcnt [3:0] and [15:14] zero, expcnt and lgkmcnt at their maximum)
+constexpr int kWaitVm0 = 0x0F70;
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -118,39 +122,6 @@ struct Lay {
     static constexpr int SET = 2 * RBYTES;
     static constexpr int BYTES = 2 * SET;
 };
-constexpr int kHalf = kTile / 2;
-
-// Per-thread staging of one streamed tile: chunk c8 of rows r and r + 16, for
-// item it = 16 r + c8 (D = 128; 8 r + c8 at D = 64) of each of two tensors.
-// Consecutive threads take consecutive chunks of a row, so the global loads
-// are whole rows.
-template <int D>
-struct Stage {
-    u32x4 x0, x1;     // tensor 1
-    u32x4 y0, y1;     // tensor 2
-};
-template <int D>
-constexpr int kItems = kHalf * (D / 8);                  // threads that copy one tile
-
-template <int D>
-__device__ __forceinline__ void stage_rows(const __bf16* __restrict__ g, int row0, int n, int tid,
-                                           u32x4& r0, u32x4& r1) {
-    const int it = tid % kItems<D>;
-    const int c8 = it % (D / 8), r = it / (D / 8);
-    const int a = min(row0 + r, n - 1), b = min(row0 + r + kHalf, n - 1);
-    r0 = *(const u32x4*)(g + (size_t)a * D + 8 * c8);
-    r1 = *(const u32x4*)(g + (size_t)b * D + 8 * c8);
-}
-
-template <int D>
-__device__ __forceinline__ void put_rows(LDS char* dst, int tid, const u32x4& r0, const u32x4& r1) {
-    if (tid >= kItems<D>) return;
-    const int c8 = tid % (D / 8), r = tid / (D / 8);
-    const int pos = 16 * (c8 ^ rswz<D>(r));
-    *(LDS u32x4*)(dst + r * 2 * D + pos) = r0;
-    *(LDS u32x4*)(dst + (r + kHalf) * 2 * D + pos) = r1;
-}
-
 // Per-lane offsets for the two operand forms of a tile.  Row operand (lane =
 // tile row l32, d = 16 ks + 8 h .. + 7): offset rowop ^ (32 ks).  Transposed
 // operand of chunk cc (lane = d 32 db + l32, tile rows {16 cc + 4 h + 0..3,
@@ -177,12 +148,61 @@ __device__ __forceinline__ bf16x8 tr_operand(const LDS char* tile, int t0, int t
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
+// Direct global-to-LDS copies of a streamed tile (buffer loads with the LDS
+// flag): no registers and no LDS store instructions.  The descriptor covers
+// one head's rows, so rows past N come back as zeros (its range check).
+// Words: base address (48 bits, stride 0), number of bytes, raw 32-bit data
+// format.  The arguments must be uniform over the wave; readfirstlane puts
+// the words in scalar registers, where the copy instruction takes them,
+// also where the compiler cannot prove the uniformity itself.
+__device__ __forceinline__ u32x4 make_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t a = (uint64_t)(uintptr_t)base;
+    u32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    r[1] = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xFFFFu);
+    r[2] = __builtin_amdgcn_readfirstlane(bytes);
+    r[3] = 0x00020000u;
+    return r;
+}
+// Lane L's 16 bytes at (descriptor base + voff + soff) go to LDS address dst
+// + 16 L (M0 holds dst; nothing else in these kernels uses M0).  Inline
+// assembly, so the compiler does not take it for an LDS write that other
+// LDS reads must wait for; completion is the caller's vmcnt wait before the
+// barrier that publishes the tile.
+__device__ __forceinline__ void dma16(LDS char* dst, u32x4 rsrc, uint32_t voff, uint32_t soff) {
+    const uint32_t m = (uint32_t)(uintptr_t)dst;
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :
+                 : "s"(m), "v"(voff), "s"(rsrc), "s"(soff)
+                 : "memory", "m0");
+}
+// One streamed tile (kTile rows from row0, uniform like dst and w) into
+// `dst` in the layout above, copied by the wave of index w of NW: copy n fills bytes [1024 n, 1024 n +
+// 1024), i.e. rows R n + L / (D/8) (R = 1024 / 2D rows per copy) at chunk
+// position L % (D/8) for lane L, which fetches the chunk that rswz puts
+// there.
+template <int D>
+constexpr int kTileCopies = kTile * 2 * D / 1024;
+template <int D, int NW>
+__device__ __forceinline__ void dma_tile(LDS char* dst, u32x4 rsrc, int row0, int w, int lane) {
+    constexpr int RC = D / 8;                 // chunks per row
+    constexpr int R = 1024 / (2 * D);         // rows per copy
+    constexpr int PER = kTileCopies<D> / NW;
+    static_assert(kTileCopies<D> % NW == 0, "copies split evenly over the waves");
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int n = w * PER + i;
+        const int r = R * n + lane / RC;
+        const uint32_t voff = (uint32_t)(r * 2 * D + 16 * ((lane % RC) ^ rswz<D>(r)));
+        dma16(dst + 1024 * n, rsrc, voff, __builtin_amdgcn_readfirstlane((uint32_t)(row0 * 2 * D)));
+    }
+}
+
 // Row statistics of the streamed query rows (dK/dV kernel): LSE * log2(e)
-// and D.  Staged raw, one step ahead like the tiles, and finished when
-// stored: any arithmetic on the loaded values at load time would make the
-// wave wait right there for every load it has in flight, the tile loads
-// issued just before included.  Rows past N get +inf (so that p = 0) and
-// D = 0.
+// and D.  Staged raw in registers, one step ahead like the tiles, and
+// finished when stored: any arithmetic on the loaded values at load time
+// would make the wave wait right there for every load it has in flight.
+// Rows past N get +inf (so that p = 0) and D = 0.
 __device__ __forceinline__ void stage_stats(const float* __restrict__ lse, const float* __restrict__ dd,
                                             int row0, int n, int tid, float& s0, float& s1, int& srow) {
     srow = row0 + (tid & 31);
@@ -272,25 +292,21 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     const int n_steps = ((CAUSAL ? min(N, r0 + kRows) : N) + kTile - 1) / kTile;
     const size_t kvhead = ((size_t)b * Hkv + hr / group) * N * D;
 
-    // Each step's copy: A = K rows, B = V rows, T = K transposed.
-    Stage<D> stg;
+    // Each step's copy, straight into LDS: A = K rows, B = V rows (K^T is
+    // read from A with transposing reads).
     const int rowop = rowop_off<D>(lane);
     const int trop0 = trop_off<D>(lane, 0), trop1 = trop_off<D>(lane, 1);
-    auto load_step = [&](int step) __attribute__((always_inline)) {
-        const int row0 = min(step, n_steps - 1) * kTile;
-        stage_rows<D>(K + kvhead, row0, N, tid, stg.x0, stg.x1);
-        stage_rows<D>(V + kvhead, row0, N, tid, stg.y0, stg.y1);
-    };
-    auto store_step = [&](int set) __attribute__((always_inline)) {
+    const u32x4 rk = make_rsrc(K + kvhead, (uint32_t)N * (2 * D));
+    const u32x4 rv = make_rsrc(V + kvhead, (uint32_t)N * (2 * D));
+    auto copy_step = [&](int step, int set) __attribute__((always_inline)) {
         LDS char* base = smem + set * L::SET;
-        put_rows<D>(base + L::A, tid, stg.x0, stg.x1);
-        put_rows<D>(base + L::B, tid, stg.y0, stg.y1);
+        dma_tile<D, kWaves>(base + L::A, rk, step * kTile, wave, lane);
+        dma_tile<D, kWaves>(base + L::B, rv, step * kTile, wave, lane);
     };
 
     // n_steps >= 1: the workgroup's first row is below N, so key tile 0 is
     // always visible.
-    load_step(0);
-    store_step(0);
+    copy_step(0, 0);
     // D of this lane's row: its 64 d (those of its dO fragments, zero past
     // N), then the other half from lane l ^ 32.  The loads of O arrived with
     // (before) the first tile's.
@@ -311,7 +327,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
     // path into the loop and waits for all loads in flight at their first
     // use in every step.
     asm volatile("" : "+v"(lse2_lane), "+v"(d_lane));
-    load_step(1);
+    __builtin_amdgcn_s_waitcnt(0);       // tile 0 (and every earlier load) has landed
+    if (n_steps > 1) copy_step(1, 1);
     __syncthreads();
 
 #pragma unroll 1
@@ -396,9 +413,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(
             for (int i = 0; i < 2 * DB; ++i) acc[i >> 1] = mfma32(ft[i], w[i & 1], acc[i >> 1]);
             reads_ahead<2 * DB, 2>();
         }
-        if (step + 1 < n_steps) store_step(set ^ 1);
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);    // this wave's copies of the next tile have landed
         __syncthreads();
-        if (step + 2 < n_steps) load_step(step + 2);
+        if (step + 2 < n_steps) copy_step(step + 2, set);
     }
 
     // Epilogue: this lane's query row, d = 32*db + 8*g + 4*h + r.
@@ -520,27 +537,29 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(
     // first tile of step st (in tiles), and its query head
     auto step_tile = [&](int st) { return t_begin + kSub<D> * (st % per_head); };
 
-    // Copies: threads 0-255 stage Q rows, 256-511 dO rows (item it = tid & 255),
-    // threads 0-63 also the row statistics (tile tid / 32 of the step).
-    const int ct = tid & 255;
-    const bool copy_do = tid >= 256;
-    u32x4 x0[kSub<D>], x1[kSub<D>];
+    // Copies of step `step` into its buffer set (step & 1): waves 0-3 copy
+    // the Q rows and waves 4-7 the dO rows straight into LDS; threads
+    // 0 .. 32 kSub - 1 stage the row statistics in registers (tile tid / 32
+    // of the step), stored with store_stats.  The statistics are loaded
+    // first, so the compiler's wait for them at the store also covers the
+    // copies issued after them.
+    const bool copy_do = wave >= 4;
     float s0 = 0.f, s1 = 0.f;
     int srow = 0;
     auto load_step = [&](int step) __attribute__((always_inline)) {
         const int st = min(step, n_steps - 1);
         const int hs = st / per_head;
         const int tile0 = step_tile(st);
-#pragma unroll
-        for (int j = 0; j < kSub<D>; ++j)
-            stage_rows<D>((copy_do ? dO : Q) + q_head(hs) * D, (tile0 + j) * kTile, N, ct, x0[j], x1[j]);
         if (tid < kSub<D> * kTile)
             stage_stats(LSE + q_head(hs), Dd + q_head(hs), (tile0 + tid / kTile) * kTile, N, tid, s0, s1, srow);
-    };
-    auto store_step = [&](int set) __attribute__((always_inline)) {
-        LDS char* base = smem + set * L::SET;
+        const u32x4 rs = make_rsrc((copy_do ? dO : Q) + q_head(hs) * D, (uint32_t)N * (2 * D));
+        LDS char* base = smem + (step & 1) * L::SET;
 #pragma unroll
-        for (int j = 0; j < kSub<D>; ++j) put_rows<D>(base + (copy_do ? L::B(j) : L::A(j)), ct, x0[j], x1[j]);
+        for (int j = 0; j < kSub<D>; ++j)
+            dma_tile<D, 4>(base + (copy_do ? L::B(j) : L::A(j)), rs, (tile0 + j) * kTile, wave & 3, lane);
+    };
+    auto store_stats = [&](int set) __attribute__((always_inline)) {
+        LDS char* base = smem + set * L::SET;
         if (tid < kSub<D> * kTile) {
             float lse2, dv;
             finish_stats(s0, s1, srow, N, lse2, dv);
@@ -552,8 +571,9 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(
 
     if (n_steps > 0) {
         load_step(0);
-        store_step(0);
-        load_step(1);
+        store_stats(0);
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);    // step 0's copies have landed
+        if (n_steps > 1) load_step(1);
     }
     __syncthreads();
 
@@ -701,7 +721,8 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(
 #pragma unroll
             for (int i = 0; i < 2 * DB; ++i) acc[i >> 1] = mfma32(ft[i], w[i & 1], acc[i >> 1]);
         }
-        if (step + 1 < n_steps) store_step(set ^ 1);
+        if (step + 1 < n_steps) store_stats(set ^ 1);
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);    // this wave's copies of the next step have landed
         __syncthreads();
         if (step + 2 < n_steps) load_step(step + 2);
     }
