@@ -66,6 +66,11 @@ CASES = [
     Workload("bwd-N1", 1, 2, 1, 1, 128, True, "bf16", 87),
     Workload("bwd-N77", 2, 1, 1, 77, 64, True, "bf16", 88),
     Workload("bwd-c3-small", 1, 2, 2, 1000, 128, True, "bf16", 89),
+    # whole dK/dV steps only (three 32-row tiles per step at d = 64, two at d = 128), and a GQA
+    # group at d = 64 whose heads each end on a full step
+    Workload("bwd-d64-whole-steps", 1, 2, 2, 192, 64, False, "bf16", 93),
+    Workload("bwd-d128-one-step", 1, 2, 2, 64, 128, True, "bf16", 94),
+    Workload("bwd-d64-gqa-whole-steps", 1, 4, 1, 288, 64, True, "bf16", 95),
 ]
 
 
